@@ -1,0 +1,232 @@
+#!/usr/bin/env python3
+"""Benchmark of the latent causal attention hot path on one MI355X.
+
+A step is one mla_latent_attn_fwd call (weight absorption, the fused causal
+latent flash kernel, the up-projection) on the long-prefill workload
+(bf16, B=2, T=16384, H=64, d=128, r=512), inputs resident in HBM.  The
+decode workload (bf16, 64 ragged sequences of 1024..8192 cached latents,
+H=32) is timed in the same run and reported in the `decode` object.
+
+Prints ONE JSON line.  `value` is prefill TFLOP/s of the absorbed method's
+algorithmic work (causal keys only); `roofline` is the flash kernel's
+achieved TFLOP/s against the dense bf16 matrix-core peak, from its
+average launch time measured with HIP events on the launch stream;
+`cpu_baseline` is the fp64 CPU oracle timed on a bounded sample of the same
+workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6     # 256 CU x 2.4 GHz x 4096 dense bf16 FLOP/clk/CU
+PEAK_HBM_GBS = 8000.0         # HBM3E
+
+
+# ---------------------------------------------------------------- algorithmic work
+def gemm_flops(M: int, K: int, N: int) -> int:
+    """FLOPs of an [M,K] x [K,N] product (one multiply and one add per term)."""
+    return 2 * M * K * N
+
+
+def prefill_flops(cfg) -> dict:
+    """Absorbed-method FLOPs of one prefill call, causal keys only."""
+    B, T, H, d, r = cfg.B, cfg.T, cfg.H, cfg.d, cfg.r
+    absorb = H * gemm_flops(B * T, d, r)
+    attn = 2 * B * H * r * T * (T + 1)          # scores + P latent over s <= t
+    up = H * gemm_flops(B * T, r, d)
+    down = gemm_flops(B * T, cfg.D, r) if cfg.D else 0
+    return {"absorb": absorb, "attn": attn, "up": up, "down": down, "total": absorb + attn + up + down}
+
+
+def decode_bytes(cfg, lens) -> dict:
+    """Algorithmic HBM bytes of one decode call: the cached latents read once,
+    both up-projection weights, q and out (bf16)."""
+    es = 2 if cfg.dtype == "bf16" else 4
+    lat = es * cfg.r * int(np.sum(lens))
+    w = 2 * es * cfg.r * cfg.H * cfg.d
+    qo = 2 * es * cfg.B * cfg.H * cfg.d
+    return {"latent": lat, "weights": w, "q_out": qo, "total": lat + w + qo}
+
+
+def prefill_row_flops(cfg, t: int) -> int:
+    """Absorbed-method FLOPs of one query row at position t."""
+    return 2 * cfg.d * cfg.r + 4 * cfg.r * (t + 1) + 2 * cfg.r * cfg.d
+
+
+# ---------------------------------------------------------------- GPU timing
+def time_steps(fn, steps: int, warmup: int):
+    import torch
+    for _ in range(warmup):
+        fn(0)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(steps):
+        fn(i)
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
+def kernel_times(fn, steps: int):
+    """Average ms per launch of each library kernel over `steps` calls (HIP events)."""
+    import torch
+    import rank_latent_causal_mla_amd as mla
+    torch.cuda.synchronize()
+    mla.mla_profile_collect()
+    mla.mla_profile_enable(True)
+    for i in range(steps):
+        fn(i)
+    torch.cuda.synchronize()
+    mla.mla_profile_enable(False)
+    stats = mla.mla_profile_collect()
+    return {k: {"avg_ms": tot / n, "launches": n} for k, (tot, n) in stats.items()}
+
+
+def bench_prefill(cfg, steps, warmup):
+    import torch
+    import synth
+    import rank_latent_causal_mla_amd as mla
+    from tests.helpers import to_device
+    inp = synth.make_inputs(cfg)
+    dev = {k: to_device(v) for k, v in inp.items()}
+    out = torch.empty_like(dev["q"])
+    dt = mla.MLA_DTYPE_BF16 if cfg.dtype == "bf16" else mla.MLA_DTYPE_F32
+    ws = torch.empty(mla.mla_latent_attn_workspace_size(cfg.B, cfg.T, cfg.H, cfg.d, cfg.r, dt),
+                     dtype=torch.uint8, device="cuda")
+
+    def step(_i):
+        mla.mla_latent_attn_fwd(dev["q"], dev["kv_latent"], dev["w_up_k"], dev["w_up_v"], out=out,
+                                scale=cfg.scale, workspace=ws)
+
+    ms = time_steps(step, steps, warmup)
+    kt = kernel_times(step, steps)
+    return ms, kt, inp
+
+
+def bench_decode(cfg, steps, warmup, copies=3):
+    """Decode with `copies` independent caches used in turn, so the 256 MB
+    last-level cache cannot hold the ~300 MB working set between steps."""
+    import torch
+    import synth
+    import rank_latent_causal_mla_amd as mla
+    from tests.helpers import to_device
+    inp = synth.make_inputs(cfg)
+    lens = inp["seq_lens"]
+    dev = {k: to_device(v) for k, v in inp.items() if k != "seq_lens"}
+    caches = [dev["kv_latent"]] + [dev["kv_latent"].clone() for _ in range(copies - 1)]
+    dlens = torch.from_numpy(lens).cuda()
+    out = torch.empty_like(dev["q"])
+    dt = mla.MLA_DTYPE_BF16
+    ws = torch.empty(mla.mla_decode_workspace_size(cfg.B, cfg.T, cfg.H, cfg.d, cfg.r, dt),
+                     dtype=torch.uint8, device="cuda")
+
+    def step(i):
+        mla.mla_decode_fwd(dev["q"], caches[i % copies], dlens, dev["w_up_k"], dev["w_up_v"], out=out,
+                           scale=cfg.scale, workspace=ws)
+
+    ms = time_steps(step, steps, warmup)
+    kt = kernel_times(step, steps)
+    return ms, kt, lens
+
+
+# ---------------------------------------------------------------- CPU baseline
+def cpu_baseline(cfg, inp, n_heads=16, n_rows=64):
+    """The fp64 oracle on a bounded sample of the prefill workload: n_rows query
+    positions spread evenly over 0..T-1 for each of n_heads heads of batch 0."""
+    import oracle
+    heads = list(range(min(n_heads, cfg.H)))
+    ts = [int(x) for x in np.linspace(0, cfg.T - 1, n_rows).round()]
+    rb = np.zeros(len(heads) * len(ts), dtype=np.int64)
+    rh = np.repeat(heads, len(ts))
+    rt = np.tile(ts, len(heads))
+    qrows = inp["q"][rb, rt, rh]
+    threads = oracle.threads(0)
+    t0 = time.perf_counter()
+    oracle.attend_rows(qrows, rb, rh, rt + 1, inp["kv_latent"], inp["w_up_k"], inp["w_up_v"], cfg.scale)
+    sec = time.perf_counter() - t0
+    flops = sum(prefill_row_flops(cfg, int(t)) for t in rt)
+    return {"value": flops / sec / 1e12, "unit": "TFLOP/s", "cores": min(threads, len(heads)),
+            "kind": "oracle", "seconds": round(sec, 3),
+            "sample": f"{len(rt)} query rows of {cfg.name}: {len(ts)} positions evenly spaced over 0..{cfg.T - 1} "
+                      f"for heads 0..{len(heads) - 1} of batch 0 (the oracle materialises k, v for the "
+                      f"{cfg.T} keys of each head); value = absorbed-method FLOPs of those rows / wall time"}
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="bf16_long_prefill")
+    ap.add_argument("--decode-workload", default="bf16_decode")
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args(argv)
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        return 2
+
+    import torch
+    import synth
+    import rank_latent_causal_mla_amd as mla
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    mla.load()
+
+    cfg = synth.CONFIGS[args.workload]
+    ms, kt, inp = bench_prefill(cfg, args.steps, args.warmup)
+    work = prefill_flops(cfg)
+    value = work["total"] / (ms * 1e-3) / 1e12
+    flash = kt.get("flash_latent_bf16")
+    roof = None
+    if flash:
+        ach = work["attn"] / (flash["avg_ms"] * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                "kernel": "flash_latent_bf16", "avg_ms": round(flash["avg_ms"], 4),
+                "flops_per_launch": work["attn"]}
+    line = {
+        "metric": "latent-attn prefill TFLOP/s (decode GB/s in `decode`) at 1 GPU, % of MFMA/HBM roofline",
+        "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": cfg.dtype, "data": "synthetic",
+        "config": {"workload": cfg.name, "B": cfg.B, "T": cfg.T, "H": cfg.H, "d": cfg.d, "r": cfg.r,
+                   "causal": True, "flops_per_step": work["total"]},
+        "roofline": roof,
+        "kernels_ms": {k: round(v["avg_ms"], 4) for k, v in kt.items()},
+    }
+    if not args.no_decode:
+        dcfg = synth.CONFIGS[args.decode_workload]
+        dms, dkt, lens = bench_decode(dcfg, max(args.steps, 10), args.warmup)
+        db = decode_bytes(dcfg, lens)
+        split = dkt.get("decode_split_bf16")
+        droof = None
+        if split:
+            ach = db["latent"] / (split["avg_ms"] * 1e-3) / 1e9
+            droof = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": None, "kernel": "decode_split_bf16",
+                     "avg_ms": round(split["avg_ms"], 4), "bytes_per_launch": db["latent"]}
+        line["decode"] = {"workload": dcfg.name, "value": round(db["total"] / (dms * 1e-3) / 1e9, 1),
+                          "unit": "GB/s", "ms_per_step": round(dms, 4), "bytes_per_step": db["total"],
+                          "sum_seq_lens": int(np.sum(lens)), "roofline": droof,
+                          "kernels_ms": {k: round(v["avg_ms"], 4) for k, v in dkt.items()}}
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(cfg, inp)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

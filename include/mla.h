@@ -1,0 +1,117 @@
+/* mla.h -- C ABI of the MI355X (gfx950) latent causal attention library.
+ *
+ * The operation (POPCORNBENCH page FW-GLM-5-1 l2_p31, the latent attention
+ * problem and its algorithm restatement): for batch b, head h, query t and
+ * every key s <= t,
+ *     k_s = kv_latent[b,s,:] @ w_up_k[:,h,:],   v_s = kv_latent[b,s,:] @ w_up_v[:,h,:],
+ *     logit_s = scale * <q[b,t,h,:], k_s>,      out[b,t,h,:] = sum_s softmax(logit)_s * v_s.
+ * The optional producer of kv_latent is the KV down-projection of
+ * POPCORNBENCH page FW-GLM-5-1 l2_p1 (its list of operations):
+ *     kv_latent = hidden @ w_down.
+ *
+ * Conventions shared by every entry point:
+ *   - Every tensor pointer is DEVICE memory owned by the caller; the library
+ *     never frees, retains or allocates it, and allocates no device memory of
+ *     its own: scratch space is the caller's `workspace`, sized by the
+ *     matching *_workspace_size query.
+ *   - Tensors are dense and row-major with the shapes given below; all float
+ *     tensors of one call share the dtype `dt` (float32 or bf16); seq_lens is
+ *     int32.  Float pointers must be 16-byte aligned.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Work is only
+ *     enqueued on it; no call synchronises the host.
+ *   - Arguments are checked before anything is enqueued.  A null pointer,
+ *     a non-positive size or misalignment returns MLA_ERR_INVALID_ARGUMENT;
+ *     a shape the kernels do not cover returns MLA_ERR_UNSUPPORTED; a
+ *     workspace smaller than required returns MLA_ERR_WORKSPACE; a failed
+ *     launch returns MLA_ERR_HIP.  mla_last_error() then describes the
+ *     failure (per calling thread).  Nothing is written on error.
+ *   - Arithmetic: float32 inputs are computed in float32; bf16 inputs use
+ *     bf16 matrix-core operands with float32 accumulation and a float32
+ *     softmax.  Results are deterministic run to run.
+ */
+#ifndef MLA_H_
+#define MLA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MLA_OK = 0,
+  MLA_ERR_INVALID_ARGUMENT = 1,
+  MLA_ERR_UNSUPPORTED = 2,
+  MLA_ERR_WORKSPACE = 3,
+  MLA_ERR_HIP = 4
+} mla_status;
+
+typedef enum { MLA_DTYPE_F32 = 0, MLA_DTYPE_BF16 = 1 } mla_dtype;
+
+/* Largest latent rank r and head dim d any path accepts. */
+#define MLA_MAX_RANK 1024
+#define MLA_MAX_HEAD_DIM 256
+
+/* KV down-projection (page FW-GLM-5-1 l2_p1, operations list):
+ *   kv_latent[b,t,:] = hidden[b,t,:] @ w_down.
+ * hidden [B,T,D], w_down [D,r] (row-major, used without transpose),
+ * kv_latent [B,T,r] (output, same dtype).  1 <= r <= MLA_MAX_RANK. */
+mla_status mla_down_proj(const void* hidden, const void* w_down, void* kv_latent,
+                         int B, int T, int D, int r, mla_dtype dt, void* stream);
+
+/* Bytes of workspace mla_latent_attn_fwd needs for this shape (0 on bad sizes). */
+size_t mla_latent_attn_workspace_size(int B, int T, int H, int d, int r, mla_dtype dt);
+
+/* Causal latent attention, prefill (page FW-GLM-5-1 l2_p31, algorithm
+ * restatement; keys s = 0..t inclusive):
+ *   q [B,T,H,d], kv_latent [B,T,r], w_up_k / w_up_v [r,H,d]  (inputs),
+ *   out [B,T,H,d] (output, dtype of q).
+ * `scale` multiplies every logit (1/sqrt(d) is the usual choice).
+ * Computed in absorbed form (q_lat = w_up_k[:,h,:] q, attention over the
+ * latents, then the w_up_v up-projection), which equals the definition up to
+ * rounding.  workspace must hold mla_latent_attn_workspace_size() bytes. */
+mla_status mla_latent_attn_fwd(const void* q, const void* kv_latent, const void* w_up_k,
+                               const void* w_up_v, void* out, int B, int T, int H, int d,
+                               int r, float scale, mla_dtype dt, void* workspace,
+                               size_t workspace_bytes, void* stream);
+
+/* Bytes of workspace mla_decode_fwd needs for this shape (0 on bad sizes). */
+size_t mla_decode_workspace_size(int B, int Tmax, int H, int d, int r, mla_dtype dt);
+
+/* Decode: one query per sequence (the same definition for the last position
+ * of a sequence of length L_b = seq_lens[b]: it attends cached latents
+ * 0..L_b-1).
+ *   q [B,1,H,d], kv_latent [B,Tmax,r] (rows >= L_b are never read),
+ *   seq_lens [B] int32 in DEVICE memory with 1 <= L_b <= Tmax,
+ *   w_up_k / w_up_v [r,H,d], out [B,1,H,d].
+ * Long caches are split over workgroups and the partial softmax states are
+ * merged by log-sum-exp.  A length outside [1, Tmax] is clamped to it (the
+ * device-resident lengths are not inspected by the host). */
+mla_status mla_decode_fwd(const void* q, const void* kv_latent, const int32_t* seq_lens,
+                          const void* w_up_k, const void* w_up_v, void* out, int B, int Tmax,
+                          int H, int d, int r, float scale, mla_dtype dt, void* workspace,
+                          size_t workspace_bytes, void* stream);
+
+/* Per-kernel timing, for benchmarking (not part of the computation).
+ * mla_profile_enable(1) makes every later kernel launch of the library record
+ * a pair of HIP events on its stream; mla_profile_enable(0) stops it.
+ * mla_profile_collect() waits for the recorded events, and returns, for each
+ * kernel name seen (up to `max`), the summed elapsed milliseconds and launch
+ * count since the previous collect; *n receives the number of entries.
+ * names[i] point to library-owned strings valid until the next collect.
+ * Not meant for concurrent use from several threads. */
+mla_status mla_profile_enable(int on);
+mla_status mla_profile_collect(const char** names, double* total_ms, int* counts, int max, int* n);
+
+/* Static description of a status code. */
+const char* mla_status_string(mla_status s);
+
+/* Detail of the last failed call on this thread ("" if none). */
+const char* mla_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_H_ */

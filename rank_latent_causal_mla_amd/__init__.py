@@ -1,0 +1,206 @@
+"""Python binding of libmla.so, the gfx950 latent causal attention library.
+
+Argument marshalling only: each function below calls the C entry point of
+the same name in include/mla.h; every step of the computation runs in the
+library's HIP kernels.  PyTorch supplies device memory and the stream.
+A missing library is an error -- there is no other implementation behind
+these names.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmla.so")
+
+MLA_OK, MLA_ERR_INVALID_ARGUMENT, MLA_ERR_UNSUPPORTED, MLA_ERR_WORKSPACE, MLA_ERR_HIP = range(5)
+MLA_DTYPE_F32, MLA_DTYPE_BF16 = 0, 1
+
+EXPORTED = ("mla_down_proj", "mla_latent_attn_workspace_size", "mla_latent_attn_fwd",
+            "mla_decode_workspace_size", "mla_decode_fwd", "mla_profile_enable", "mla_profile_collect",
+            "mla_status_string", "mla_last_error")
+
+_lib = None
+
+
+class MLAError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        super().__init__(f"{status_string(status)}: {detail}")
+        self.status = status
+
+
+def load():
+    """Load libmla.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with rank_latent_causal_mla_amd.build.build()")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i32, f32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    lib.mla_down_proj.restype = i32
+    lib.mla_down_proj.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, vp]
+    lib.mla_latent_attn_workspace_size.restype = sz
+    lib.mla_latent_attn_workspace_size.argtypes = [i32] * 6
+    lib.mla_latent_attn_fwd.restype = i32
+    lib.mla_latent_attn_fwd.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, i32, vp, sz, vp]
+    lib.mla_decode_workspace_size.restype = sz
+    lib.mla_decode_workspace_size.argtypes = [i32] * 6
+    lib.mla_decode_fwd.restype = i32
+    lib.mla_decode_fwd.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, i32, vp, sz, vp]
+    lib.mla_status_string.restype = ctypes.c_char_p
+    lib.mla_status_string.argtypes = [i32]
+    lib.mla_last_error.restype = ctypes.c_char_p
+    lib.mla_last_error.argtypes = []
+    lib.mla_profile_enable.restype = i32
+    lib.mla_profile_enable.argtypes = [i32]
+    lib.mla_profile_collect.restype = i32
+    lib.mla_profile_collect.argtypes = [ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(ctypes.c_double),
+                                        ctypes.POINTER(ctypes.c_int), i32, ctypes.POINTER(ctypes.c_int)]
+    _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load().mla_status_string(status).decode()
+
+
+def last_error() -> str:
+    return load().mla_last_error().decode()
+
+
+def _check(status: int):
+    if status != MLA_OK:
+        raise MLAError(status, last_error())
+
+
+# ---- raw C ABI (plain integers / pointers)
+
+def mla_down_proj_raw(hidden, w_down, kv_latent, B, T, D, r, dt, stream=0):
+    return load().mla_down_proj(hidden, w_down, kv_latent, B, T, D, r, dt, stream)
+
+
+def mla_latent_attn_workspace_size(B, T, H, d, r, dt):
+    return int(load().mla_latent_attn_workspace_size(B, T, H, d, r, dt))
+
+
+def mla_decode_workspace_size(B, Tmax, H, d, r, dt):
+    return int(load().mla_decode_workspace_size(B, Tmax, H, d, r, dt))
+
+
+def mla_latent_attn_fwd_raw(q, kv_latent, w_up_k, w_up_v, out, B, T, H, d, r, scale, dt, ws, ws_bytes, stream=0):
+    return load().mla_latent_attn_fwd(q, kv_latent, w_up_k, w_up_v, out, B, T, H, d, r, scale, dt, ws,
+                                      ws_bytes, stream)
+
+
+def mla_decode_fwd_raw(q, kv_latent, seq_lens, w_up_k, w_up_v, out, B, Tmax, H, d, r, scale, dt, ws,
+                       ws_bytes, stream=0):
+    return load().mla_decode_fwd(q, kv_latent, seq_lens, w_up_k, w_up_v, out, B, Tmax, H, d, r, scale, dt, ws,
+                                 ws_bytes, stream)
+
+
+def mla_profile_enable(on: bool = True):
+    _check(load().mla_profile_enable(1 if on else 0))
+
+
+def mla_profile_collect(max_entries: int = 64) -> dict:
+    """{kernel name: (total ms, launches)} since the previous collect."""
+    names = (ctypes.c_char_p * max_entries)()
+    tot = (ctypes.c_double * max_entries)()
+    cnt = (ctypes.c_int * max_entries)()
+    n = ctypes.c_int(0)
+    _check(load().mla_profile_collect(names, tot, cnt, max_entries, ctypes.byref(n)))
+    return {names[i].decode(): (tot[i], cnt[i]) for i in range(n.value) if cnt[i]}
+
+
+# ---- torch-tensor marshalling (same names as the C entry points)
+
+def _dt(t):
+    import torch
+    if t.dtype == torch.float32:
+        return MLA_DTYPE_F32
+    if t.dtype == torch.bfloat16:
+        return MLA_DTYPE_BF16
+    raise TypeError(f"unsupported dtype {t.dtype} (float32 or bfloat16)")
+
+
+def _stream(stream):
+    import torch
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return getattr(stream, "cuda_stream", stream)
+
+
+def _dev(*ts):
+    for t in ts:
+        if not t.is_cuda:
+            raise ValueError("tensors must be on the GPU")
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+
+
+def mla_down_proj(hidden, w_down, kv_latent=None, stream=None):
+    """kv_latent[B,T,r] = hidden[B,T,D] @ w_down[D,r]."""
+    import torch
+    _dev(hidden, w_down)
+    B, T, D = hidden.shape
+    r = w_down.shape[1]
+    if kv_latent is None:
+        kv_latent = torch.empty((B, T, r), dtype=hidden.dtype, device=hidden.device)
+    _dev(kv_latent)
+    _check(mla_down_proj_raw(hidden.data_ptr(), w_down.data_ptr(), kv_latent.data_ptr(), B, T, D, r,
+                             _dt(hidden), _stream(stream)))
+    return kv_latent
+
+
+def mla_latent_attn_fwd(q, kv_latent, w_up_k, w_up_v, out=None, scale=None, workspace=None, stream=None):
+    """Causal latent attention, prefill: q[B,T,H,d], kv_latent[B,T,r], w_up_k/w_up_v[r,H,d] -> out[B,T,H,d]."""
+    import torch
+    _dev(q, kv_latent, w_up_k, w_up_v)
+    B, T, H, d = q.shape
+    r = kv_latent.shape[-1]
+    dt = _dt(q)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    nbytes = mla_latent_attn_workspace_size(B, T, H, d, r, dt)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    _dev(out, workspace)
+    _check(mla_latent_attn_fwd_raw(q.data_ptr(), kv_latent.data_ptr(), w_up_k.data_ptr(), w_up_v.data_ptr(),
+                                   out.data_ptr(), B, T, H, d, r, float(scale), dt, workspace.data_ptr(),
+                                   workspace.numel() * workspace.element_size(), _stream(stream)))
+    return out
+
+
+def mla_decode_fwd(q, kv_latent, seq_lens, w_up_k, w_up_v, out=None, scale=None, workspace=None, stream=None):
+    """Decode: q[B,1,H,d], kv_latent[B,Tmax,r], seq_lens[B] int32 (device) -> out[B,1,H,d]."""
+    import torch
+    _dev(q, kv_latent, seq_lens, w_up_k, w_up_v)
+    if seq_lens.dtype != torch.int32:
+        raise TypeError("seq_lens must be int32")
+    B, Tmax, r = kv_latent.shape
+    H, d = w_up_k.shape[1], w_up_k.shape[2]
+    dt = _dt(q)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    nbytes = mla_decode_workspace_size(B, Tmax, H, d, r, dt)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    _dev(out, workspace)
+    _check(mla_decode_fwd_raw(q.data_ptr(), kv_latent.data_ptr(), seq_lens.data_ptr(), w_up_k.data_ptr(),
+                              w_up_v.data_ptr(), out.data_ptr(), B, Tmax, H, d, r, float(scale), dt,
+                              workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                              _stream(stream)))
+    return out
+
+
+def full_path(hidden, w_down, q, w_up_k, w_up_v, scale=None, stream=None):
+    """hidden -> kv_latent (mla_down_proj) -> causal latent attention (mla_latent_attn_fwd)."""
+    lat = mla_down_proj(hidden, w_down, stream=stream)
+    return mla_latent_attn_fwd(q, lat, w_up_k, w_up_v, scale=scale, stream=stream)

@@ -1,0 +1,177 @@
+// C ABI of the library: argument checks, workspace sizing, path selection
+// and launch sequencing.  Declarations and the contract are in include/mla.h.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "../../include/mla.h"
+#include "mla_kernels.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+mla_status fail(mla_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+mla_status ok() {
+  g_last_error.clear();
+  return MLA_OK;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+constexpr double kLog2e = 1.4426950408889634;
+
+// Shared size checks of the attention entry points.
+mla_status check_dims(int B, int T, int H, int d, int r, mla_dtype dt, const char* tname) {
+  if (B < 1 || T < 1 || H < 1 || d < 1 || r < 1)
+    return fail(MLA_ERR_INVALID_ARGUMENT, "sizes must be positive (B=%d %s=%d H=%d d=%d r=%d)", B,
+                tname, T, H, d, r);
+  if (dt != MLA_DTYPE_F32 && dt != MLA_DTYPE_BF16)
+    return fail(MLA_ERR_INVALID_ARGUMENT, "unknown dtype %d", (int)dt);
+  if (r > MLA_MAX_RANK) return fail(MLA_ERR_UNSUPPORTED, "r=%d exceeds %d", r, MLA_MAX_RANK);
+  if (d > MLA_MAX_HEAD_DIM) return fail(MLA_ERR_UNSUPPORTED, "d=%d exceeds %d", d, MLA_MAX_HEAD_DIM);
+  // element counts are indexed with 64-bit offsets, block counts must fit the grid
+  const double rows = (double)B * T * H;
+  if ((double)B * T >= 2147483647.0 || rows * (r > d ? r : d) >= 9.0e15)
+    return fail(MLA_ERR_UNSUPPORTED, "problem too large (B*T*H=%.0f)", rows);
+  return MLA_OK;
+}
+
+bool use_mfma(mla_dtype dt, int d, int r) { return dt == MLA_DTYPE_BF16 && mla::mfma_supported(d, r); }
+
+mla_status device_lds_limit(size_t* bytes) {
+  int dev = 0, v = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerBlock, dev);
+  if (e != hipSuccess) return fail(MLA_ERR_HIP, "device query failed: %s", hipGetErrorString(e));
+  *bytes = (size_t)v;
+  return MLA_OK;
+}
+
+mla_status launched(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(MLA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* mla_status_string(mla_status s) {
+  switch (s) {
+    case MLA_OK: return "ok";
+    case MLA_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case MLA_ERR_UNSUPPORTED: return "unsupported shape";
+    case MLA_ERR_WORKSPACE: return "workspace too small";
+    case MLA_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+const char* mla_last_error(void) { return g_last_error.c_str(); }
+
+mla_status mla_down_proj(const void* hidden, const void* w_down, void* kv_latent, int B, int T,
+                         int D, int r, mla_dtype dt, void* stream) {
+  if (!hidden || !w_down || !kv_latent) return fail(MLA_ERR_INVALID_ARGUMENT, "null pointer");
+  if (B < 1 || T < 1 || D < 1 || r < 1)
+    return fail(MLA_ERR_INVALID_ARGUMENT, "sizes must be positive (B=%d T=%d D=%d r=%d)", B, T, D, r);
+  if (dt != MLA_DTYPE_F32 && dt != MLA_DTYPE_BF16)
+    return fail(MLA_ERR_INVALID_ARGUMENT, "unknown dtype %d", (int)dt);
+  if (!aligned16(hidden) || !aligned16(w_down) || !aligned16(kv_latent))
+    return fail(MLA_ERR_INVALID_ARGUMENT, "pointers must be 16-byte aligned");
+  if (r > MLA_MAX_RANK) return fail(MLA_ERR_UNSUPPORTED, "r=%d exceeds %d", r, MLA_MAX_RANK);
+  if ((double)B * T >= 2147483647.0 / 64 || (double)B * T * D >= 9.0e15)
+    return fail(MLA_ERR_UNSUPPORTED, "problem too large");
+  return launched(mla::down_proj(dt == MLA_DTYPE_BF16, hidden, w_down, kv_latent, B * T, D, r,
+                                 (hipStream_t)stream),
+                  "down_proj launch");
+}
+
+size_t mla_latent_attn_workspace_size(int B, int T, int H, int d, int r, mla_dtype dt) {
+  if (B < 1 || T < 1 || H < 1 || d < 1 || r < 1) return 0;
+  if (dt != MLA_DTYPE_F32 && dt != MLA_DTYPE_BF16) return 0;
+  return use_mfma(dt, d, r) ? mla::prefill_mfma_workspace(B, T, H, d, r)
+                            : mla::prefill_simt_workspace(B, T, H, d, r);
+}
+
+mla_status mla_latent_attn_fwd(const void* q, const void* kv_latent, const void* w_up_k,
+                               const void* w_up_v, void* out, int B, int T, int H, int d, int r,
+                               float scale, mla_dtype dt, void* workspace, size_t workspace_bytes,
+                               void* stream) {
+  if (!q || !kv_latent || !w_up_k || !w_up_v || !out || !workspace)
+    return fail(MLA_ERR_INVALID_ARGUMENT, "null pointer");
+  mla_status s = check_dims(B, T, H, d, r, dt, "T");
+  if (s != MLA_OK) return s;
+  if (!std::isfinite(scale)) return fail(MLA_ERR_INVALID_ARGUMENT, "scale must be finite");
+  if (!aligned16(q) || !aligned16(kv_latent) || !aligned16(w_up_k) || !aligned16(w_up_v) ||
+      !aligned16(out) || !aligned16(workspace))
+    return fail(MLA_ERR_INVALID_ARGUMENT, "pointers must be 16-byte aligned");
+  const size_t need = mla_latent_attn_workspace_size(B, T, H, d, r, dt);
+  if (workspace_bytes < need)
+    return fail(MLA_ERR_WORKSPACE, "workspace %zu bytes < %zu required", workspace_bytes, need);
+  hipStream_t st = (hipStream_t)stream;
+  if (use_mfma(dt, d, r))
+    return launched(mla::prefill_mfma(q, kv_latent, w_up_k, w_up_v, out, B, T, H, d, r,
+                                      (float)(scale * kLog2e), workspace, st),
+                    "prefill launch");
+  return launched(mla::prefill_simt(dt == MLA_DTYPE_BF16, q, kv_latent, w_up_k, w_up_v, out, B, T,
+                                    H, d, r, scale, workspace, st),
+                  "prefill launch");
+}
+
+size_t mla_decode_workspace_size(int B, int Tmax, int H, int d, int r, mla_dtype dt) {
+  if (B < 1 || Tmax < 1 || H < 1 || d < 1 || r < 1) return 0;
+  if (dt != MLA_DTYPE_F32 && dt != MLA_DTYPE_BF16) return 0;
+  return use_mfma(dt, d, r) ? mla::decode_mfma_workspace(B, Tmax, H, d, r)
+                            : mla::decode_simt_workspace(B, Tmax, H, d, r);
+}
+
+mla_status mla_decode_fwd(const void* q, const void* kv_latent, const int32_t* seq_lens,
+                          const void* w_up_k, const void* w_up_v, void* out, int B, int Tmax,
+                          int H, int d, int r, float scale, mla_dtype dt, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  if (!q || !kv_latent || !seq_lens || !w_up_k || !w_up_v || !out || !workspace)
+    return fail(MLA_ERR_INVALID_ARGUMENT, "null pointer");
+  mla_status s = check_dims(B, Tmax, H, d, r, dt, "Tmax");
+  if (s != MLA_OK) return s;
+  if (!std::isfinite(scale)) return fail(MLA_ERR_INVALID_ARGUMENT, "scale must be finite");
+  if (!aligned16(q) || !aligned16(kv_latent) || !aligned16(w_up_k) || !aligned16(w_up_v) ||
+      !aligned16(out) || !aligned16(workspace) || ((uintptr_t)seq_lens & 3u))
+    return fail(MLA_ERR_INVALID_ARGUMENT, "pointers must be 16-byte aligned (seq_lens 4-byte)");
+  const size_t need = mla_decode_workspace_size(B, Tmax, H, d, r, dt);
+  if (workspace_bytes < need)
+    return fail(MLA_ERR_WORKSPACE, "workspace %zu bytes < %zu required", workspace_bytes, need);
+  hipStream_t st = (hipStream_t)stream;
+  if (use_mfma(dt, d, r)) {
+    size_t limit = 0;
+    s = device_lds_limit(&limit);
+    if (s != MLA_OK) return s;
+    if (mla::decode_lds_bytes(r) > limit)
+      return fail(MLA_ERR_UNSUPPORTED, "decode needs %zu bytes of LDS per block, device allows %zu",
+                  mla::decode_lds_bytes(r), limit);
+    return launched(mla::decode_mfma(q, kv_latent, seq_lens, w_up_k, w_up_v, out, B, Tmax, H, d, r,
+                                     (float)(scale * kLog2e), workspace, st),
+                    "decode launch");
+  }
+  return launched(mla::decode_simt(dt == MLA_DTYPE_BF16, q, kv_latent, seq_lens, w_up_k, w_up_v,
+                                   out, B, Tmax, H, d, r, scale, workspace, st),
+                  "decode launch");
+}
+
+}  // extern "C"
+
+namespace mla {
+bool mfma_supported(int d, int r) {
+  return (r == 128 || r == 256 || r == 512) && d % 32 == 0 && d <= 256;
+}
+}  // namespace mla

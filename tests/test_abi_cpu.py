@@ -1,0 +1,95 @@
+"""The C ABI on a host without a GPU: the library loads, exports what
+include/mla.h declares, and rejects bad arguments before touching a device."""
+import os
+import re
+
+import pytest
+
+import rank_latent_causal_mla_amd as mla
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+F32, BF16 = mla.MLA_DTYPE_F32, mla.MLA_DTYPE_BF16
+P = 1 << 20   # a 16-byte aligned fake address: never dereferenced on these paths
+
+
+def declared_symbols():
+    text = open(os.path.join(ROOT, "include", "mla.h")).read()
+    return sorted(set(re.findall(r"^\s*(?:mla_status|size_t|const char\*)\s+(mla_\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_abi():
+    assert declared_symbols() == sorted(mla.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = mla.load()
+    for name in declared_symbols():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings():
+    assert mla.status_string(mla.MLA_OK) == "ok"
+    for s in range(1, 5):
+        assert mla.status_string(s) not in ("", "ok", "unknown status")
+    assert mla.status_string(99) == "unknown status"
+
+
+def attn(**kw):
+    a = dict(q=P, kv=P, wk=P, wv=P, out=P, B=2, T=64, H=4, d=32, r=32, scale=0.17, dt=F32, ws=P, wsb=1 << 40)
+    a.update(kw)
+    return mla.mla_latent_attn_fwd_raw(a["q"], a["kv"], a["wk"], a["wv"], a["out"], a["B"], a["T"], a["H"], a["d"],
+                                       a["r"], a["scale"], a["dt"], a["ws"], a["wsb"])
+
+
+def dec(**kw):
+    a = dict(q=P, kv=P, lens=P, wk=P, wv=P, out=P, B=2, T=64, H=4, d=32, r=32, scale=0.17, dt=F32, ws=P,
+             wsb=1 << 40)
+    a.update(kw)
+    return mla.mla_decode_fwd_raw(a["q"], a["kv"], a["lens"], a["wk"], a["wv"], a["out"], a["B"], a["T"], a["H"],
+                                  a["d"], a["r"], a["scale"], a["dt"], a["ws"], a["wsb"])
+
+
+@pytest.mark.parametrize("fn", [attn, dec])
+@pytest.mark.parametrize("kw,status", [
+    ({"q": 0}, mla.MLA_ERR_INVALID_ARGUMENT),
+    ({"out": 0}, mla.MLA_ERR_INVALID_ARGUMENT),
+    ({"ws": 0}, mla.MLA_ERR_INVALID_ARGUMENT),
+    ({"B": 0}, mla.MLA_ERR_INVALID_ARGUMENT),
+    ({"T": -1}, mla.MLA_ERR_INVALID_ARGUMENT),
+    ({"H": 0}, mla.MLA_ERR_INVALID_ARGUMENT),
+    ({"d": 0}, mla.MLA_ERR_INVALID_ARGUMENT),
+    ({"r": 0}, mla.MLA_ERR_INVALID_ARGUMENT),
+    ({"dt": 7}, mla.MLA_ERR_INVALID_ARGUMENT),
+    ({"scale": float("nan")}, mla.MLA_ERR_INVALID_ARGUMENT),
+    ({"q": P + 2}, mla.MLA_ERR_INVALID_ARGUMENT),
+    ({"r": 2048}, mla.MLA_ERR_UNSUPPORTED),
+    ({"d": 512}, mla.MLA_ERR_UNSUPPORTED),
+    ({"wsb": 7}, mla.MLA_ERR_WORKSPACE),
+])
+def test_argument_errors(fn, kw, status):
+    assert fn(**kw) == status
+    assert mla.last_error() != ""
+
+
+def test_decode_null_lengths():
+    assert dec(lens=0) == mla.MLA_ERR_INVALID_ARGUMENT
+    assert dec(lens=P + 2) == mla.MLA_ERR_INVALID_ARGUMENT
+
+
+def test_down_proj_errors():
+    assert mla.mla_down_proj_raw(0, P, P, 1, 1, 1, 1, F32) == mla.MLA_ERR_INVALID_ARGUMENT
+    assert mla.mla_down_proj_raw(P, P, P, 1, 0, 1, 1, F32) == mla.MLA_ERR_INVALID_ARGUMENT
+    assert mla.mla_down_proj_raw(P, P, P, 1, 1, 1, 1, 3) == mla.MLA_ERR_INVALID_ARGUMENT
+    assert mla.mla_down_proj_raw(P, P + 4, P, 1, 1, 1, 1, F32) == mla.MLA_ERR_INVALID_ARGUMENT
+    assert mla.mla_down_proj_raw(P, P, P, 1, 1, 1, 4096, F32) == mla.MLA_ERR_UNSUPPORTED
+
+
+def test_workspace_sizes():
+    # float32 path: q_lat and o_lat in float32
+    assert mla.mla_latent_attn_workspace_size(2, 64, 4, 32, 32, F32) == 2 * 2 * 64 * 4 * 32 * 4
+    # bf16 matrix-core path: q_lat, o_lat in bf16 plus W_uv^T
+    rows = 8 * 2048 * 16
+    assert mla.mla_latent_attn_workspace_size(8, 2048, 16, 128, 512, BF16) == (2 * rows * 512 + 16 * 128 * 512) * 2
+    assert mla.mla_latent_attn_workspace_size(0, 1, 1, 1, 1, F32) == 0
+    assert mla.mla_decode_workspace_size(64, 8192, 32, 128, 512, BF16) > 64 * 32 * 512 * 4
+    assert mla.mla_decode_workspace_size(1, 1, 1, 1, 1, 9) == 0

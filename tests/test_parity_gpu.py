@@ -1,0 +1,226 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 CPU oracle on
+the same seeded inputs (|gpu - oracle| <= atol + rtol |oracle|; 1e-4 for
+float32 storage, 2e-2 for bf16 storage with float32 accumulation)."""
+import dataclasses
+
+import numpy as np
+import pytest
+
+import oracle
+import rank_latent_causal_mla_amd as mla
+import synth
+from tests.helpers import compare, to_device, to_f64
+
+pytestmark = pytest.mark.gpu
+
+
+def tight(got, ref, limit=4e-3):
+    """A bar well inside the stated one: the relative RMS error over the sampled
+    outputs.  bf16 rounding of q_lat, P, o_lat and the output gives ~2e-3; a
+    systematic error (a wrong scale, a dropped key) gives far more."""
+    got = np.asarray(got, dtype=np.float64)
+    rel = np.sqrt(np.mean((got - ref) ** 2) / np.mean(ref ** 2))
+    print(f"relative rms error {rel:.3e}")
+    assert rel < limit, rel
+
+
+def cfg_like(name, **kw):
+    return dataclasses.replace(synth.CONFIGS[name], **kw)
+
+
+def run_prefill(cfg, inp):
+    import torch
+    dev = {k: to_device(v) for k, v in inp.items() if k != "seq_lens"}
+    if cfg.D:
+        lat = mla.mla_down_proj(dev["hidden"], dev["w_down"])
+    else:
+        lat = dev["kv_latent"]
+    out = mla.mla_latent_attn_fwd(dev["q"], lat, dev["w_up_k"], dev["w_up_v"], scale=cfg.scale)
+    torch.cuda.synchronize()
+    return out, lat
+
+
+def oracle_prefill(cfg, inp):
+    if cfg.D:
+        return oracle.full_path(inp["hidden"], inp["w_down"], inp["q"], inp["w_up_k"], inp["w_up_v"], cfg.scale)
+    return oracle.latent_attn(inp["q"], inp["kv_latent"], inp["w_up_k"], inp["w_up_v"], cfg.scale)
+
+
+# ---------------------------------------------------------------- prefill, whole outputs
+SMALL = [
+    ("fp32_small", {}),
+    ("page_attn_size", {}),                                    # r = 24: non-multiple-of-16 tails
+    ("page_kv_size_h8", {}),                                   # full path, r = 48
+    ("page_kv_size_h1", {}),                                   # full path, H = 1, d = 128
+    ("bf16_prefill", dict(B=2, T=100, H=16)),                  # ragged key tail, several tiles
+    ("bf16_prefill", dict(B=1, T=70, H=3)),                    # rows per block not a multiple of H
+    ("bf16_prefill", dict(B=3, T=1, H=5)),                     # single key
+    ("bf16_prefill", dict(B=1, T=33, H=64, r=256)),            # r = 256 kernels
+    ("bf16_prefill", dict(B=2, T=65, H=2, r=128, d=64)),       # r = 128, d = 64
+    ("bf16_prefill", dict(B=1, T=40, H=4, r=48, d=16)),        # bf16 outside the matrix-core tiles
+    ("fp32_small", dict(T=129, r=512, d=128, H=2)),            # float32 at the wide latent
+]
+
+
+@pytest.mark.parametrize("name,kw", SMALL, ids=[f"{n}-{i}" for i, (n, _) in enumerate(SMALL)])
+def test_prefill_matches_oracle(name, kw):
+    cfg = cfg_like(name, **kw)
+    inp = synth.make_inputs(cfg)
+    print(f"prefill parity {cfg}", flush=True)
+    out, _ = run_prefill(cfg, inp)
+    ref = oracle_prefill(cfg, inp)
+    err = compare(to_f64(out), ref, cfg.dtype, cfg.name)
+    print(f"max abs err {err:.3e}")
+
+
+def test_full_path_config():
+    cfg = synth.CONFIGS["fp32_full_path"]
+    inp = synth.make_inputs(cfg)
+    out, lat = run_prefill(cfg, inp)
+    compare(to_f64(lat), oracle.down_proj(inp["hidden"], inp["w_down"]), "f32", "down-projection")
+    ref = oracle_prefill(cfg, inp)
+    err = compare(to_f64(out), ref, "f32", "full path")
+    print(f"fp32 full path max abs err {err:.3e}")
+
+
+# ---------------------------------------------------------------- prefill at full size, sampled rows
+def sampled_prefill(cfg, heads, rows_per_head, seed=1):
+    import torch
+    inp = synth.make_inputs(cfg)
+    print(f"full-size prefill {cfg.name}", flush=True)
+    out, _ = run_prefill(cfg, inp)
+    out = out.float()
+    assert torch.isfinite(out).all().item()
+    rng = np.random.default_rng(seed)
+    T = cfg.T
+    fixed = [0, 1, 31, 32, 33, 127, 128, T // 2, T - 2, T - 1]
+    rb, rh, rt = [], [], []
+    for (b, h) in heads:
+        ts = sorted(set(fixed + list(rng.integers(0, T, rows_per_head))))
+        for t in ts:
+            rb.append(b); rh.append(h); rt.append(t)
+    rb, rh, rt = map(np.array, (rb, rh, rt))
+    q = inp["q"]
+    qrows = q[rb, rt, rh]
+    ref = oracle.attend_rows(qrows, rb, rh, rt + 1, inp["kv_latent"], inp["w_up_k"], inp["w_up_v"], cfg.scale)
+    got = to_f64(out[torch.from_numpy(rb).cuda(), torch.from_numpy(rt).cuda(), torch.from_numpy(rh).cuda()])
+    err = compare(got, ref, cfg.dtype, cfg.name)
+    print(f"{cfg.name}: {len(rb)} sampled rows, max abs err {err:.3e}")
+    tight(got, ref)
+    return out
+
+
+def test_bf16_prefill_full_size_sampled():
+    sampled_prefill(synth.CONFIGS["bf16_prefill"], heads=[(0, 0), (3, 7), (7, 15)], rows_per_head=24)
+
+
+def test_bf16_long_prefill_full_size_sampled():
+    sampled_prefill(synth.CONFIGS["bf16_long_prefill"], heads=[(0, 0), (1, 63)], rows_per_head=12)
+
+
+# ---------------------------------------------------------------- decode
+def run_decode(cfg, inp, lens, pad_nan=False):
+    import torch
+    dev = {k: to_device(v) for k, v in inp.items() if k != "seq_lens"}
+    lat = dev["kv_latent"]
+    if pad_nan:
+        lat = lat.clone()
+        for b, L in enumerate(lens):
+            lat[b, int(L):] = float("nan")
+    out = mla.mla_decode_fwd(dev["q"], lat, torch.from_numpy(np.asarray(lens, np.int32)).cuda(),
+                             dev["w_up_k"], dev["w_up_v"], scale=cfg.scale)
+    torch.cuda.synchronize()
+    return out
+
+
+DECODE_SMALL = [
+    ("bf16_decode", dict(B=6, T=300, H=32), [1, 32, 33, 100, 299, 300]),
+    ("bf16_decode", dict(B=3, T=2100, H=8), [1025, 2100, 1024]),       # splits, partial last split
+    ("bf16_decode", dict(B=2, T=64, H=40), [64, 7]),                   # two head groups, ragged
+    ("bf16_decode", dict(B=2, T=50, H=4, r=48, d=16), [50, 1]),        # outside matrix-core tiles
+    ("fp32_small", dict(B=3, T=70, decode=True), [70, 1, 33]),         # float32 decode
+]
+
+
+@pytest.mark.parametrize("name,kw,lens", DECODE_SMALL, ids=[f"{n}-{i}" for i, (n, _, _) in enumerate(DECODE_SMALL)])
+def test_decode_matches_oracle(name, kw, lens):
+    cfg = cfg_like(name, **kw)
+    inp = synth.make_inputs(cfg)
+    print(f"decode parity {cfg} lens={lens}", flush=True)
+    out = run_decode(cfg, inp, lens, pad_nan=True)    # rows past each length are NaN and must not be read
+    ref = oracle.decode(inp["q"], inp["kv_latent"], lens, inp["w_up_k"], inp["w_up_v"], cfg.scale)
+    err = compare(to_f64(out), ref, cfg.dtype, "decode")
+    print(f"max abs err {err:.3e}")
+
+
+def test_decode_full_size_sampled():
+    cfg = synth.CONFIGS["bf16_decode"]
+    inp = synth.make_inputs(cfg)
+    lens = inp["seq_lens"]
+    print(f"full-size decode, sum L = {int(lens.sum())}", flush=True)
+    out = to_f64(run_decode(cfg, inp, lens))
+    assert np.isfinite(out).all()
+    # every sequence at heads 0 and 31, and every head of the shortest and longest sequence
+    pairs = {(b, h) for b in range(cfg.B) for h in (0, cfg.H - 1)}
+    for b in (int(np.argmin(lens)), int(np.argmax(lens))):
+        pairs |= {(b, h) for h in range(cfg.H)}
+    rb = np.array([p[0] for p in sorted(pairs)])
+    rh = np.array([p[1] for p in sorted(pairs)])
+    qrows = inp["q"][rb, 0, rh]
+    ref = oracle.attend_rows(qrows, rb, rh, lens[rb], inp["kv_latent"], inp["w_up_k"], inp["w_up_v"], cfg.scale)
+    err = compare(out[rb, 0, rh], ref, "bf16", "decode full size")
+    print(f"decode: {len(rb)} (b, h) rows, max abs err {err:.3e}")
+    tight(out[rb, 0, rh], ref)
+
+
+def test_decode_equals_last_prefill_row():
+    import torch
+    cfg = cfg_like("bf16_prefill", B=2, T=200, H=16)
+    inp = synth.make_inputs(cfg)
+    pre, _ = run_prefill(cfg, inp)
+    lens = [200, 77]
+    q = np.stack([inp["q"][0, 199], inp["q"][1, 76]])[:, None]
+    dinp = dict(inp, q=q)
+    dec = run_decode(cfg_like("bf16_decode", B=2, T=200, H=16), dinp, lens)
+    a = to_f64(dec)[:, 0]
+    b = np.stack([to_f64(pre[0, 199]), to_f64(pre[1, 76])])
+    assert np.abs(a - b).max() < 1e-2
+
+
+# ---------------------------------------------------------------- properties
+def test_causality_bitwise():
+    import torch
+    cfg = cfg_like("bf16_prefill", B=1, T=96, H=16)
+    inp = synth.make_inputs(cfg)
+    base, _ = run_prefill(cfg, inp)
+    t0 = 40
+    inp2 = dict(inp)
+    lat = inp["kv_latent"].copy()
+    lat[:, t0 + 1:] = synth.normal_tensor(99, 2, lat[:, t0 + 1:].shape, 3.0, "bf16")
+    inp2["kv_latent"] = lat
+    pert, _ = run_prefill(cfg, inp2)
+    assert torch.equal(base[:, :t0 + 1], pert[:, :t0 + 1])
+    assert not torch.equal(base[:, t0 + 1:], pert[:, t0 + 1:])
+
+
+def test_deterministic():
+    import torch
+    cfg = cfg_like("bf16_prefill", B=2, T=130, H=16)
+    inp = synth.make_inputs(cfg)
+    a, _ = run_prefill(cfg, inp)
+    b, _ = run_prefill(cfg, inp)
+    assert torch.equal(a, b)
+    dcfg = cfg_like("bf16_decode", B=4, T=1500, H=32)
+    dinp = synth.make_inputs(dcfg)
+    lens = [1500, 3, 1024, 1025]
+    assert torch.equal(run_decode(dcfg, dinp, lens), run_decode(dcfg, dinp, lens))
+
+
+def test_first_row_is_v0():
+    cfg = cfg_like("bf16_prefill", B=2, T=8, H=16)
+    inp = synth.make_inputs(cfg)
+    out, _ = run_prefill(cfg, inp)
+    lat = synth.bf16_bits_to_f32(inp["kv_latent"]).astype(np.float64)
+    wv = synth.bf16_bits_to_f32(inp["w_up_v"]).astype(np.float64)
+    v0 = np.einsum("br,rhe->bhe", lat[:, 0], wv)
+    compare(to_f64(out[:, 0]), v0, "bf16", "row 0 = v_0")
