@@ -29,6 +29,31 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2516.6     # 256 CU x 2.4 GHz x 4096 dense bf16 FLOP/clk/CU
 PEAK_HBM_GBS = 8000.0         # HBM3E
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+
+
+def library_source_sha() -> str:
+    import glob
+    import hashlib
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(ROOT, "rank_latent_causal_mla_amd", "csrc", "*"))):
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel: str):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
+    summary, or None when the library sources changed since it was taken."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            t = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_sha256_16") != library_source_sha():
+        return None
+    k = t.get("kernels", {}).get(kernel)
+    return None if k is None else int(k["hbm_bytes"])
 
 
 # ---------------------------------------------------------------- algorithmic work
@@ -171,6 +196,8 @@ def main(argv=None):
     ap.add_argument("--decode-workload", default="bf16_decode")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run a plain 1 GiB device copy (reference for HBM byte counters)")
     args = ap.parse_args(argv)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -185,6 +212,14 @@ def main(argv=None):
         return 2
     mla.load()
 
+    if args.calibrate_copy:
+        src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")   # 1 GiB
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
     cfg = synth.CONFIGS[args.workload]
     ms, kt, inp = bench_prefill(cfg, args.steps, args.warmup)
     work = prefill_flops(cfg)
@@ -194,7 +229,7 @@ def main(argv=None):
     if flash:
         ach = work["attn"] / (flash["avg_ms"] * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": measured_traffic("flash_latent_bf16"),
                 "kernel": "flash_latent_bf16", "avg_ms": round(flash["avg_ms"], 4),
                 "flops_per_launch": work["attn"]}
     line = {
@@ -216,7 +251,8 @@ def main(argv=None):
         if split:
             ach = db["latent"] / (split["avg_ms"] * 1e-3) / 1e9
             droof = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": None, "kernel": "decode_split_bf16",
+                     "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": measured_traffic("decode_split_bf16"),
+                     "kernel": "decode_split_bf16",
                      "avg_ms": round(split["avg_ms"], 4), "bytes_per_launch": db["latent"]}
         line["decode"] = {"workload": dcfg.name, "value": round(db["total"] / (dms * 1e-3) / 1e9, 1),
                           "unit": "GB/s", "ms_per_step": round(dms, 4), "bytes_per_step": db["total"],
