@@ -11,8 +11,12 @@ SOURCES = ["mla_api.hip", "kernels_mfma.hip", "kernels_simt.hip", "profile.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 # -packed-fp32-ops: no v_pk_{add,mul,fma}_f32 in any kernel.
+# -amdgpu-mfma-vgpr-form: matrix instructions written with the builtins keep
+# their accumulators in VGPRs; the flash kernels pin their large output
+# accumulators to AGPRs explicitly (inline asm), so the two never compete.
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-shared", "-fPIC",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         "-mllvm", "-amdgpu-mfma-vgpr-form=true",
          "-I", os.path.join(ROOT, "include")]
 
 

@@ -25,15 +25,16 @@ namespace mla {
 __device__ __forceinline__ int swz(int s) { return ((s & 3) << 2) | ((s >> 2) & 3); }
 
 // ---------------------------------------------------------------------------
-// Absorption: q_lat[n*H + h, rho] = sum_e W_uk[rho, h, e] * q[n, h, e]
-// (n = b*T + t).  Computed transposed, q_lat^T = W_h q_h^T, so each lane
+// Absorption: q_lat[n*H + h, rho] = qscale * sum_e W_uk[rho, h, e] * q[n, h, e]
+// (n = b*T + t; qscale folds the softmax scale into q_lat when the consumer
+// wants pre-scaled scores, else 1).  Computed transposed, q_lat^T = W_h q_h^T, so each lane
 // ends with 4 consecutive rho of one query row.  Block: 4 waves; wave w
 // covers rho in [w R/4, (w+1) R/4) for 32 tokens of one head.
 template <int R>
 __global__ __launch_bounds__(256) void absorb_bf16(const uint16_t* __restrict__ q,
                                                    const uint16_t* __restrict__ wk,
                                                    uint16_t* __restrict__ q_lat, int N, int H,
-                                                   int d) {
+                                                   int d, float qscale) {
   constexpr int NB = R / 128;  // 32-row blocks of rho per wave
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int g = lane >> 5, l32 = lane & 31;
@@ -61,8 +62,8 @@ __global__ __launch_bounds__(256) void absorb_bf16(const uint16_t* __restrict__ 
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int rho = rho0 + 32 * i + 8 * j + 4 * g;
-      u32x2 v = {pack_bf16x2(acc[i][4 * j], acc[i][4 * j + 1]),
-                 pack_bf16x2(acc[i][4 * j + 2], acc[i][4 * j + 3])};
+      u32x2 v = {pack_bf16x2(acc[i][4 * j] * qscale, acc[i][4 * j + 1] * qscale),
+                 pack_bf16x2(acc[i][4 * j + 2] * qscale, acc[i][4 * j + 3] * qscale)};
       *(u32x2*)(orow + rho) = v;
     }
 }
@@ -270,21 +271,230 @@ __device__ __forceinline__ void dma_tile(const uint16_t* latb, int k0, int nkeys
 
 // ---------------------------------------------------------------------------
 // Causal latent flash attention, prefill.
-// q_lat, o_lat: [B][T*H][R] bf16 (row t*H + h of batch b); lat: [B][T][R] bf16.
-// One block = 128 consecutive (t, h) rows of one batch = 4 waves x 32 rows;
-// every wave streams the same latent tiles 0 .. t_max (double-buffered in
-// LDS), so one tile load serves all heads in the block.  Blocks are issued
-// heaviest (largest t) first.
+//
+// The two products need the latent tile in two orientations: the scores
+// contract over rho (rows of L, rho-contiguous) and P * L contracts over keys
+// (columns of L).  Transposing in LDS (ds_read_b64_tr_b16) is far slower than
+// plain 16-byte reads, so the tile also comes pre-transposed from a per-call
+// copy of the latents, latT [B][ceil(T/32)][R][32] (latent_transpose below),
+// whose 32 keys per row are stored in the order the P operand holds them.
+// Both orientations are copied into LDS by LDS-DMA and read with ds_read_b128.
+
+// Transposed tiles.  The P operand built from the score accumulators gives
+// lane group G (lanes 16 G .. 16 G + 15) the keys {4 G + u, 16 + 4 G + u},
+// u = 0..3, as its 8 k-slots.  The transposed copy of a 32-key tile is
+// therefore stored group-major, [G][rho][8]: entry u of (G, rho) holds
+// latent[key(G, u)][rho] with key(G, u) = 16 (u / 4) + 4 G + u % 4, so each
+// lane reads its A operand as one contiguous 16-byte chunk and the 16 lanes
+// of a group read 256 contiguous bytes.
+__device__ __forceinline__ int tkey(int G, int u) { return 16 * (u >> 2) + 4 * G + (u & 3); }
+
+// lat [B][T][R] -> latT [B][nt][4][R][8], nt = ceil(T / 32); keys >= T are zero.
+template <int R>
+__global__ __launch_bounds__(256) void latent_transpose(const uint16_t* __restrict__ lat,
+                                                        uint16_t* __restrict__ latT, int T, int nt) {
+  __shared__ __attribute__((aligned(16))) uint16_t s[32][R + 8];
+  const int tile = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+  constexpr int NC = R / 8;
+  const uint16_t* src = lat + ((size_t)b * T + 32 * tile) * R;
+  for (int idx = tid; idx < 32 * NC; idx += 256) {
+    const int key = idx / NC, c = idx % NC;
+    const u32x4 v = 32 * tile + key < T ? *(const u32x4*)(src + (size_t)key * R + 8 * c) : u32x4{0, 0, 0, 0};
+    *(u32x4*)&s[key][8 * c] = v;
+  }
+  __syncthreads();
+  uint16_t* dst = latT + ((size_t)b * nt + tile) * R * 32;
+  for (int idx = tid; idx < 4 * R; idx += 256) {
+    const int G = idx / R, rho = idx % R;
+    uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      w[i] = (uint32_t)s[tkey(G, 2 * i)][rho] | ((uint32_t)s[tkey(G, 2 * i + 1)][rho] << 16);
+    *(u32x4*)(dst + (size_t)idx * 8) = u32x4{w[0], w[1], w[2], w[3]};
+  }
+}
+
+// Row-major LDS tile for the scores: key row s keeps 16-byte chunk c at
+// position c ^ (s & 15) within its aligned group of 16, so the reads of one
+// chunk by 16 consecutive key rows (one pass of a 16-byte LDS read) hit 16
+// distinct 16-byte bank groups.  The copy is 32 * R * 2 / 1024 LDS-DMA
+// instructions of 1 KB (lane i lands at base + 16 i); wave w (wave-uniform)
+// issues instructions w, w + 4, ...  Keys past nkeys-1 re-read row nkeys-1.
+template <int R>
+__device__ __forceinline__ void dma_rowtile(const uint16_t* latb, int k0, int nkeys, char* tile, int w) {
+  constexpr int NC = R / 8;
+  constexpr int NINSTR = 32 * R * 2 / 1024;
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int i = 0; i < NINSTR / 4; ++i) {
+    const int k = 4 * i + w;
+    const int idx = k * 64 + lane;
+    const int s = idx / NC, p = idx % NC;
+    const int c = (p & ~15) | ((p & 15) ^ (s & 15));
+    const int key = k0 + s < nkeys ? k0 + s : nkeys - 1;
+    __builtin_amdgcn_global_load_lds(
+        (const __attribute__((address_space(1))) void*)(latb + (size_t)key * R + 8 * c),
+        (__attribute__((address_space(3))) void*)(uintptr_t)(tile + k * 1024), 16, 0, 0);
+  }
+}
+
+// Transposed tile: a straight copy of its [4][R][8] image (R * 64 bytes).
+template <int R>
+__device__ __forceinline__ void dma_tileT(const uint16_t* src, char* tbuf, int w) {
+  constexpr int NINSTR = R * 64 / 1024;
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int i = 0; i < NINSTR / 4; ++i) {
+    const int k = 4 * i + w;
+    __builtin_amdgcn_global_load_lds(
+        (const __attribute__((address_space(1))) void*)((const char*)src + k * 1024 + 16 * lane),
+        (__attribute__((address_space(3))) void*)(uintptr_t)(tbuf + k * 1024), 16, 0, 0);
+  }
+}
+
+// Wait until at most n of this wave's vector-memory operations (here: the
+// LDS-DMA copies, in issue order) are still outstanding.
+template <int n>
+__device__ __forceinline__ void wait_vmem_outstanding() {
+  static_assert(n >= 0 && n < 64, "vmcnt range");
+  // s_waitcnt fields: vmcnt[3:0] and [15:14], expcnt[6:4], lgkmcnt[11:8]
+  __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Per-wave tile math of the prefill kernel on 16x16x32 matrix instructions.
+// Lane l = 16 G + n.  The wave's 32 query rows form two blocks qb (rows
+// 16 qb + n); a 32-key tile forms two key blocks kb.
+//   scores:  S^T[16 kb + 4 G + v][16 qb + n] in s[kb][qb][v]   (A = L rows, B = q_lat^T)
+//   P:       lane keeps, per qb, the 8 probabilities of its keys
+//            {16 kb + 4 G + v}: k-slot 8 G + 4 kb + v of the P^T operand.
+//   output:  O^T[16 c + 4 G + v][16 qb + n] in o[c][qb][v]      (A = L^T, B = P^T)
+// so each lane holds two query rows, and a row's keys sit in the four lanes
+// n + 16 G'.
+template <int R>
+struct Flash {
+  static constexpr int NKS = R / 32;  // 32-wide steps of the rho contraction
+  static constexpr int NOB = R / 16;  // 16-row blocks of output columns
+
+  // Four independent accumulator chains keep the matrix unit busy.
+  static __device__ __forceinline__ void scores(const char* rowtile, const bf16x8 (*qf)[NKS],
+                                                f32x4 (&s)[2][2]) {
+    const int lane = threadIdx.x & 63;
+    const int G = lane >> 4, n = lane & 15;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) s[kb][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // read i = 2 ks + kb: key row 16 kb + n, chunk 4 ks + G (swizzled by the row)
+    auto addr = [&](int i) {
+      const int kb = i & 1, ks = i >> 1;
+      const int key = 16 * kb + n, c = 4 * ks + G;
+      return (const bf16x8*)(rowtile + key * (R * 2) + 16 * ((c & ~15) | ((c & 15) ^ (key & 15))));
+    };
+    constexpr int NR = 2 * NKS, DEPTH = 3;  // LDS reads kept in flight ahead of their use
+    bf16x8 ring[DEPTH];
+#pragma unroll
+    for (int i = 0; i < DEPTH; ++i) ring[i] = *addr(i);
+#pragma unroll
+    for (int i = 0; i < NR; ++i) {
+      const bf16x8 av = ring[i % DEPTH];
+      if (i + DEPTH < NR) ring[i % DEPTH] = *addr(i + DEPTH);
+      const int kb = i & 1, ks = i >> 1;
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) s[kb][qb] = mfma16x16x32(av, qf[qb][ks], s[kb][qb]);
+      // keep each read DEPTH steps ahead of its use; vector ops may move freely
+      __builtin_amdgcn_sched_barrier(0x0002 | 0x0400);
+    }
+  }
+
+  // Online-softmax update of both query rows of the lane for one tile.  The
+  // scores are already in log2 units (q_lat carries scale * log2 e).
+  // lim[qb]: keys with offset 16 kb + v (from k0 + 4 G) above lim are masked.
+  static __device__ __forceinline__ void softmax(const f32x4 (&s)[2][2], const int (&lim)[2],
+                                                 float (&m_run)[2], float (&l_run)[2], float (&alpha)[2],
+                                                 bool& grow_any, bf16x8 (&P)[2]) {
+    grow_any = false;
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      float x[8];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) x[4 * kb + v] = (16 * kb + v > lim[qb]) ? -INFINITY : s[kb][qb][v];
+      float mt = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])), fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
+      mt = max_xor32(max_xor16(mt));
+      const bool grow = mt > m_run[qb] + kRescaleSlack;
+      alpha[qb] = grow ? exp2f(m_run[qb] - mt) : 1.f;
+      m_run[qb] = grow ? mt : m_run[qb];
+      grow_any |= grow;
+      const float msub = m_run[qb] == -INFINITY ? 0.f : m_run[qb];
+      float ps = 0.f;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const float p = exp2f(x[u] - msub);
+        ps += p;
+        P[qb][u] = (__bf16)p;
+      }
+      l_run[qb] = l_run[qb] * alpha[qb] + ps;
+    }
+  }
+
+  static __device__ __forceinline__ void rescale(f32x4 (&o)[NOB][2], const float (&alpha)[2]) {
+    mfma_agpr_wait();
+#pragma unroll
+    for (int c = 0; c < NOB; ++c)
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {  // a few registers at a time
+        mfma_agpr_tie(o[c][qb]);
+        o[c][qb] *= alpha[qb];
+        mfma_agpr_tie(o[c][qb]);
+      }
+  }
+
+  // O^T += L^T P^T from the transposed tile ([4][R][8] image).
+  static __device__ __forceinline__ void pv(const char* ttile, bf16x8 (&P)[2], f32x4 (&o)[NOB][2]) {
+    const int lane = threadIdx.x & 63;
+    const int G = lane >> 4, n = lane & 15;
+    const char* pa = ttile + G * (R * 16) + 16 * n;
+    constexpr int DEPTH = 4;  // LDS reads kept in flight ahead of their use
+    bf16x8 ring[DEPTH];
+#pragma unroll
+    for (int i = 0; i < DEPTH; ++i) ring[i] = *(const bf16x8*)(pa + 256 * i);
+    mfma_operand_ready(P[0]);
+    mfma_operand_ready(P[1]);
+#pragma unroll
+    for (int c = 0; c < NOB; ++c) {
+      const bf16x8 av = ring[c % DEPTH];
+      if (c + DEPTH < NOB) ring[c % DEPTH] = *(const bf16x8*)(pa + 256 * (c + DEPTH));
+      mfma16x16x32_a(o[c][0], av, P[0]);
+      mfma16x16x32_a(o[c][1], av, P[1]);
+    }
+  }
+};
+
+// q_lat, o_lat: [B][T*H][R] bf16 (row t*H + h of batch b; q_lat pre-scaled by
+// scale * log2 e); lat: [B][T][R];
+// latT: [B][ceil(T/32)][R][32] (latent_transpose).  One block = 128
+// consecutive (t, h) rows of one batch = 4 waves x 32 rows; all heads in the
+// block share each latent tile.  Per tile j the wave computes the softmax of
+// tile j while the scores of tile j+1 run on the matrix unit, then P_j L_j.
+// Row-major tiles (two buffers) and transposed tiles (three buffers) are
+// both copied two tiles ahead.  Blocks are issued heaviest (largest t) first.
 template <int R>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
 void flash_latent_bf16(const uint16_t* __restrict__ q_lat, const uint16_t* __restrict__ lat,
-                       uint16_t* __restrict__ o_lat, int B, int T, int H, float sl2) {
+                       const uint16_t* __restrict__ latT, uint16_t* __restrict__ o_lat, int B,
+                       int T, int H) {
+  using F = Flash<R>;
   constexpr int TILE_BYTES = 32 * R * 2;
-  __shared__ __attribute__((aligned(16))) char smem[2 * TILE_BYTES];
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int g = lane >> 5, l32 = lane & 31;
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  char* rowbuf = smem;                      // [2][TILE_BYTES]
+  char* tbuf = smem + 2 * TILE_BYTES;       // [3][TILE_BYTES]
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
+  const int G = lane >> 4, n = lane & 15;
   const long TH = (long)T * H;
   const int nrb = (int)((TH + 127) / 128);
+  const int nt = (T + 31) / 32;
   const int rb = nrb - 1 - (int)(blockIdx.x / B);
   const int b = blockIdx.x % B;
   const long row0 = (long)rb * 128;
@@ -295,52 +505,101 @@ void flash_latent_bf16(const uint16_t* __restrict__ q_lat, const uint16_t* __res
   const bool wactive = wrow0 < TH;
   const int t_first_w = wactive ? (int)(wrow0 / H) : 0;
   const int t_last_w = wactive ? (int)(((TH < wrow0 + 32 ? TH : wrow0 + 32) - 1) / H) : -1;
-  const long my_row = wrow0 + l32;
-  const long crow = my_row < TH ? my_row : TH - 1;
-  const int t_row = (int)(crow / H);
-
-  bf16x8 qf[TileMath<R>::NKK];
-  {
-    const uint16_t* qrow = q_lat + ((size_t)b * TH + crow) * R + 8 * g;
+  long my_row[2];
+  int t_row[2];
 #pragma unroll
-    for (int kk = 0; kk < TileMath<R>::NKK; ++kk) qf[kk] = *(const bf16x8*)(qrow + 16 * kk);
+  for (int qb = 0; qb < 2; ++qb) {
+    my_row[qb] = wrow0 + 16 * qb + n;
+    const long crow = my_row[qb] < TH ? my_row[qb] : TH - 1;
+    t_row[qb] = (int)(crow / H);
   }
-  f32x16 o[TileMath<R>::NOB];
+
+  bf16x8 qf[2][F::NKS];
 #pragma unroll
-  for (int c = 0; c < TileMath<R>::NOB; ++c) o[c] = f32x16{};
-  float m_run = -INFINITY, l_run = 0.f;
+  for (int qb = 0; qb < 2; ++qb) {
+    const long crow = my_row[qb] < TH ? my_row[qb] : TH - 1;
+    const uint16_t* qrow = q_lat + ((size_t)b * TH + crow) * R + 8 * G;
+#pragma unroll
+    for (int ks = 0; ks < F::NKS; ++ks) qf[qb][ks] = *(const bf16x8*)(qrow + 32 * ks);
+  }
+  f32x4 o[F::NOB][2];
+#pragma unroll
+  for (int c = 0; c < F::NOB; ++c) o[c][0] = o[c][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
 
   const uint16_t* latb = lat + (size_t)b * T * R;
-  dma_tile<R>(latb, 0, T, smem, w, 4);
+  const uint16_t* latTb = latT + (size_t)b * nt * R * 32;
+  dma_rowtile<R>(latb, 0, T, rowbuf, w);
+  dma_tileT<R>(latTb, tbuf, w);
+  if (ntiles > 1) {
+    dma_rowtile<R>(latb, 32, T, rowbuf + TILE_BYTES, w);
+    dma_tileT<R>(latTb + (size_t)R * 32, tbuf + TILE_BYTES, w);
+  }
   wait_all_memory();
   __syncthreads();
+  f32x4 s_cur[2][2];
+  F::scores(rowbuf, qf, s_cur);
+  __syncthreads();  // row tile 0 is refilled below
   for (int j = 0; j < ntiles; ++j) {
-    const int buf = j & 1;
-    if (j + 1 < ntiles) dma_tile<R>(latb, 32 * (j + 1), T, smem + (buf ^ 1) * TILE_BYTES, w, 4);
+    // tiles j+2 (both orientations) are copied during this iteration; at
+    // its end only the copies issued one iteration earlier must have landed
+    const bool ahead = j + 2 < ntiles;
+    if (ahead) {
+      dma_tileT<R>(latTb + (size_t)(j + 2) * R * 32, tbuf + ((j + 2) % 3) * TILE_BYTES, w);
+      dma_rowtile<R>(latb, 32 * (j + 2), T, rowbuf + (j & 1) * TILE_BYTES, w);
+    }
     const int k0 = 32 * j;
-    if (k0 <= t_last_w)
-      TileMath<R>::step(smem + buf * TILE_BYTES, k0, qf, o, m_run, l_run, t_row,
-                        k0 + 31 > t_first_w, sl2);
-    wait_all_memory();
-    __syncthreads();
+    const bool act = k0 <= t_last_w;
+    const bool need_mask = k0 + 31 > t_first_w;
+    int lim[2];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) lim[qb] = need_mask ? t_row[qb] - k0 - 4 * G : 1 << 30;
+    // Softmax of tile j (vector ALU) next to the scores of tile j+1 (matrix
+    // unit).  Both run unconditionally: a tile past the wave's rows is fully
+    // masked (p = 0, state unchanged); the scores after the last tile read a
+    // stale buffer and are discarded.
+    bf16x8 P[2];
+    float alpha[2];
+    bool grow_any;
+    F::softmax(s_cur, lim, m_run, l_run, alpha, grow_any, P);
+    f32x4 s_next[2][2];
+    F::scores(rowbuf + ((j + 1) & 1) * TILE_BYTES, qf, s_next);
+    if (act) {
+      if (__builtin_amdgcn_ballot_w64(grow_any)) F::rescale(o, alpha);
+      F::pv(tbuf + (j % 3) * TILE_BYTES, P, o);
+    }
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) s_cur[kb][qb] = s_next[kb][qb];
+    if (ahead)
+      wait_vmem_outstanding<2 * (32 * R * 2 / 1024 / 4)>();  // tiles j+2 may stay in flight
+    else
+      wait_all_memory();
+    // a bare barrier: __syncthreads() would also wait for the copy still in flight
+    __builtin_amdgcn_s_barrier();
   }
   if (!wactive) return;
   mfma_agpr_wait();
 #pragma unroll
-  for (int c = 0; c < TileMath<R>::NOB; ++c) mfma_agpr_tie(o[c]);
-  const float lt = l_run + __shfl_xor(l_run, 32);
-  const float inv = 1.f / lt;
-  if (my_row >= TH) return;
-  uint16_t* orow = o_lat + ((size_t)b * TH + my_row) * R;
+  for (int c = 0; c < F::NOB; ++c) {
+    mfma_agpr_tie(o[c][0]);
+    mfma_agpr_tie(o[c][1]);
+  }
 #pragma unroll
-  for (int c = 0; c < TileMath<R>::NOB; ++c)
+  for (int qb = 0; qb < 2; ++qb) {
+    float lt = l_run[qb] + __shfl_xor(l_run[qb], 16);
+    lt += __shfl_xor(lt, 32);
+    const float inv = 1.f / lt;
+    if (my_row[qb] >= TH) continue;
+    uint16_t* orow = o_lat + ((size_t)b * TH + my_row[qb]) * R + 4 * G;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int rho = 32 * c + 8 * j + 4 * g;
-      u32x2 v = {pack_bf16x2(o[c][4 * j] * inv, o[c][4 * j + 1] * inv),
-                 pack_bf16x2(o[c][4 * j + 2] * inv, o[c][4 * j + 3] * inv)};
-      *(u32x2*)(orow + rho) = v;
+    for (int c = 0; c < F::NOB; ++c) {
+      u32x2 v = {pack_bf16x2(o[c][qb][0] * inv, o[c][qb][1] * inv),
+                 pack_bf16x2(o[c][qb][2] * inv, o[c][qb][3] * inv)};
+      *(u32x2*)(orow + 16 * c) = v;
     }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -493,21 +752,34 @@ template <int R>
 static hipError_t run_prefill(const uint16_t* q, const uint16_t* lat, const uint16_t* wk,
                               const uint16_t* wv, uint16_t* out, int B, int T, int H, int d,
                               float sl2, uint16_t* q_lat, uint16_t* o_lat, uint16_t* wvT,
-                              hipStream_t st) {
+                              uint16_t* latT, hipStream_t st) {
   const int N = B * T;
+  const int nt = (T + 31) / 32;
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute((const void*)flash_latent_bf16<R>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)flash_lds_bytes(R));
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
   {
     ProfScope ps("absorb_bf16", st);
-    hipLaunchKernelGGL(absorb_bf16<R>, dim3((N + 31) / 32, H), dim3(256), 0, st, q, wk, q_lat, N, H, d);
+    hipLaunchKernelGGL(absorb_bf16<R>, dim3((N + 31) / 32, H), dim3(256), 0, st, q, wk, q_lat, N, H, d, sl2);
   }
   {
     ProfScope ps("transpose_wv", st);
     hipLaunchKernelGGL(transpose_wv, dim3((R + 31) / 32, (d + 31) / 32, H), dim3(256), 0, st, wv, wvT, R, H, d);
   }
+  {
+    ProfScope ps("latent_transpose", st);
+    hipLaunchKernelGGL(latent_transpose<R>, dim3(nt, B), dim3(256), 0, st, lat, latT, T, nt);
+  }
   const long TH = (long)T * H;
   const int nrb = (int)((TH + 127) / 128);
   {
     ProfScope ps("flash_latent_bf16", st);
-    hipLaunchKernelGGL(flash_latent_bf16<R>, dim3(B * nrb), dim3(256), 0, st, q_lat, lat, o_lat, B, T, H, sl2);
+    hipLaunchKernelGGL(flash_latent_bf16<R>, dim3(B * nrb), dim3(256), flash_lds_bytes(R), st, q_lat,
+                       lat, latT, o_lat, B, T, H);
   }
   {
     ProfScope ps("up_bf16", st);
@@ -534,7 +806,7 @@ static hipError_t run_decode(const uint16_t* q, const uint16_t* lat, const int32
   }
   {
     ProfScope ps("absorb_bf16", st);
-    hipLaunchKernelGGL(absorb_bf16<R>, dim3((B + 31) / 32, H), dim3(256), 0, st, q, wk, q_lat, B, H, d);
+    hipLaunchKernelGGL(absorb_bf16<R>, dim3((B + 31) / 32, H), dim3(256), 0, st, q, wk, q_lat, B, H, d, 1.f);
   }
   {
     ProfScope ps("transpose_wv", st);
@@ -562,8 +834,9 @@ hipError_t prefill_mfma(const void* q, const void* lat, const void* wk, const vo
   uint16_t* q_lat = (uint16_t*)ws;
   uint16_t* o_lat = q_lat + rows * r;
   uint16_t* wvT = o_lat + rows * r;
+  uint16_t* latT = wvT + (size_t)H * d * r;
 #define ARGS (const uint16_t*)q, (const uint16_t*)lat, (const uint16_t*)wk, (const uint16_t*)wv, \
-             (uint16_t*)out, B, T, H, d, sl2, q_lat, o_lat, wvT, st
+             (uint16_t*)out, B, T, H, d, sl2, q_lat, o_lat, wvT, latT, st
   switch (r) {
     case 128: return run_prefill<128>(ARGS);
     case 256: return run_prefill<256>(ARGS);
@@ -575,7 +848,8 @@ hipError_t prefill_mfma(const void* q, const void* lat, const void* wk, const vo
 
 size_t prefill_mfma_workspace(int B, int T, int H, int d, int r) {
   const size_t rows = (size_t)B * T * H;
-  return (2 * rows * r + (size_t)H * d * r) * 2;
+  const size_t nt = ((size_t)T + 31) / 32;
+  return (2 * rows * r + (size_t)H * d * r + (size_t)B * nt * 32 * r) * 2;
 }
 
 int decode_nsplit(int Tmax) {

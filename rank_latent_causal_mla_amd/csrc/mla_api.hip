@@ -120,6 +120,14 @@ mla_status mla_latent_attn_fwd(const void* q, const void* kv_latent, const void*
   if (workspace_bytes < need)
     return fail(MLA_ERR_WORKSPACE, "workspace %zu bytes < %zu required", workspace_bytes, need);
   hipStream_t st = (hipStream_t)stream;
+  if (use_mfma(dt, d, r)) {
+    size_t limit = 0;
+    s = device_lds_limit(&limit);
+    if (s != MLA_OK) return s;
+    if (mla::flash_lds_bytes(r) > limit)
+      return fail(MLA_ERR_UNSUPPORTED, "prefill needs %zu bytes of LDS per block, device allows %zu",
+                  mla::flash_lds_bytes(r), limit);
+  }
   if (use_mfma(dt, d, r))
     return launched(mla::prefill_mfma(q, kv_latent, w_up_k, w_up_v, out, B, T, H, d, r,
                                       (float)(scale * kLog2e), workspace, st),

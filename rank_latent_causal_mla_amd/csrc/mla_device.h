@@ -53,6 +53,30 @@ __device__ __forceinline__ void mfma_operand_ready(bf16x8& v) {
 __device__ __forceinline__ void mfma_agpr_wait() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 4"); }
 __device__ __forceinline__ void mfma_agpr_tie(f32x16& c) { asm volatile("" : "+a"(c)); }
 
+// D[16x16] += A[16x32] * B[32x16] in fp32, bf16 operands.  Lane l supplies
+// A[l%16][8(l/16)+0..7] and B[8(l/16)+0..7][l%16]; element v of the result
+// is D[4(l/16) + v][l%16].
+__device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+// Accumulator pinned to AGPRs (same rules as mfma32x32x16_a).
+// Not volatile: a side-effect-free asm lets loads be scheduled across it.
+__device__ __forceinline__ void mfma16x16x32_a(f32x4& c, bf16x8 a, bf16x8 b) {
+  asm("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma_agpr_tie(f32x4& c) { asm volatile("" : "+a"(c)); }
+
+// Max of v over lanes l and l ^ 32 (v_permlane32_swap: no LDS round trip).
+__device__ __forceinline__ float max_xor32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+// Max of v over lanes l and l ^ 16 (v_permlane16_swap exchanges 16-lane rows).
+__device__ __forceinline__ float max_xor16(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
 // LDS transpose read: within each group of 16 lanes, element k of lane i is
 // element i%4 of the 8 bytes addressed by lane 4k + i/4.
 __device__ __forceinline__ i16x4 lds_read_tr16(const void* lds_byte_addr) {

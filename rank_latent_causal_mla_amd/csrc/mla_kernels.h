@@ -13,6 +13,9 @@ constexpr int kDecodeTilesPerWave = 8;
 // the end for two wave states plus their (m, l).
 constexpr size_t decode_lds_bytes(int R) { return (size_t)4 * 32 * R * 2 + 2 * 64 * 2 * 4; }
 
+// LDS of the prefill flash kernel: two row-major and three transposed 32-key tiles.
+constexpr size_t flash_lds_bytes(int R) { return (size_t)5 * 32 * R * 2; }
+
 // ---- bf16 matrix-core path (r in {128, 256, 512}, d % 32 == 0, d <= 256)
 bool mfma_supported(int d, int r);
 hipError_t prefill_mfma(const void* q, const void* lat, const void* wk, const void* wv, void* out,
