@@ -246,13 +246,13 @@ def main(argv=None):
         dcfg = synth.CONFIGS[args.decode_workload]
         dms, dkt, lens = bench_decode(dcfg, max(args.steps, 10), args.warmup)
         db = decode_bytes(dcfg, lens)
-        split = dkt.get("decode_split_bf16")
+        split = dkt.get("decode_split")
         droof = None
         if split:
             ach = db["latent"] / (split["avg_ms"] * 1e-3) / 1e9
             droof = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": measured_traffic("decode_split_bf16"),
-                     "kernel": "decode_split_bf16",
+                     "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": measured_traffic("decode_split"),
+                     "kernel": "decode_split",
                      "avg_ms": round(split["avg_ms"], 4), "bytes_per_launch": db["latent"]}
         line["decode"] = {"workload": dcfg.name, "value": round(db["total"] / (dms * 1e-3) / 1e9, 1),
                           "unit": "GB/s", "ms_per_step": round(dms, 4), "bytes_per_step": db["total"],

@@ -1,6 +1,6 @@
-// gfx950 matrix-core kernels of the bf16 path: weight absorption, the fused
-// causal latent flash kernel, the decode split-K kernel with its log-sum-exp
-// merge, and the per-head up-projection.
+// gfx950 matrix-core kernels of the bf16 prefill path: weight absorption, the
+// fused causal latent flash kernel and the per-head up-projection (the decode
+// kernels are in kernels_decode.hip).
 //
 // The attention they compute is the latent causal attention of POPCORNBENCH
 // page FW-GLM-5-1 l2_p31 (algorithm restatement), rewritten by bilinearity:
@@ -17,43 +17,40 @@
 
 namespace mla {
 
-// XOR swizzle of the 16-byte chunks of one latent row in LDS.  Row s keeps
-// its chunks, permuted within each aligned group of 16 by f(s); f is a
-// bijection on 0..15 chosen so that (a) the 16-byte reads of one chunk from
-// 16 consecutive rows, and (b) the transpose reads of 4 consecutive rows x 4
-// consecutive chunks, both hit distinct LDS banks.
-__device__ __forceinline__ int swz(int s) { return ((s & 3) << 2) | ((s >> 2) & 3); }
-
 // ---------------------------------------------------------------------------
 // Absorption: q_lat[n*H + h, rho] = qscale * sum_e W_uk[rho, h, e] * q[n, h, e]
-// (n = b*T + t; qscale folds the softmax scale into q_lat when the consumer
-// wants pre-scaled scores, else 1).  Computed transposed, q_lat^T = W_h q_h^T, so each lane
-// ends with 4 consecutive rho of one query row.  Block: 4 waves; wave w
-// covers rho in [w R/4, (w+1) R/4) for 32 tokens of one head.
-template <int R>
+// (n = b*T + t; qscale folds the softmax scale and log2 e into q_lat for the
+// flash kernel).  Computed transposed, q_lat^T = W_h q_h^T, so each lane ends
+// with 4 consecutive rho of one query row.  Block: 4 waves; wave w covers rho
+// in [w R/4, (w+1) R/4) for 32 tokens of one head.  DK = d / 16 steps of the
+// contraction, all operands of a step loaded before its matrix ops.
+template <int R, int DK>
 __global__ __launch_bounds__(256) void absorb_bf16(const uint16_t* __restrict__ q,
                                                    const uint16_t* __restrict__ wk,
                                                    uint16_t* __restrict__ q_lat, int N, int H,
-                                                   int d, float qscale) {
+                                                   float qscale) {
   constexpr int NB = R / 128;  // 32-row blocks of rho per wave
+  constexpr int d = 16 * DK;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int g = lane >> 5, l32 = lane & 31;
   const int h = blockIdx.y;
   const int n = blockIdx.x * 32 + l32;
   const int nc = min(n, N - 1);
   const int rho0 = w * (R / 4);
+  const uint16_t* qrow = q + ((size_t)nc * H + h) * d + 8 * g;
+  bf16x8 bq[DK];
+#pragma unroll
+  for (int ks = 0; ks < DK; ++ks) bq[ks] = *(const bf16x8*)(qrow + 16 * ks);
   f32x16 acc[NB];
 #pragma unroll
-  for (int i = 0; i < NB; ++i) acc[i] = f32x16{};
-  const uint16_t* qrow = q + ((size_t)nc * H + h) * d + 8 * g;
-  for (int ks = 0; ks < d / 16; ++ks) {
-    const bf16x8 bq = *(const bf16x8*)(qrow + 16 * ks);
+  for (int i = 0; i < NB; ++i) {
+    const uint16_t* wrow = wk + ((size_t)(rho0 + 32 * i + l32) * H + h) * d + 8 * g;
+    bf16x8 a[DK];
 #pragma unroll
-    for (int i = 0; i < NB; ++i) {
-      const int rho = rho0 + 32 * i + l32;
-      const bf16x8 a = *(const bf16x8*)(wk + ((size_t)rho * H + h) * d + 16 * ks + 8 * g);
-      acc[i] = mfma32x32x16(a, bq, acc[i]);
-    }
+    for (int ks = 0; ks < DK; ++ks) a[ks] = *(const bf16x8*)(wrow + 16 * ks);
+    acc[i] = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < DK; ++ks) acc[i] = mfma32x32x16(a[ks], bq[ks], acc[i]);
   }
   if (n >= N) return;
   uint16_t* orow = q_lat + ((size_t)n * H + h) * R;
@@ -84,6 +81,36 @@ __global__ void transpose_wv(const uint16_t* __restrict__ wv, uint16_t* __restri
     const int e = e0 + k, rho = rho0 + tx;
     if (e < d && rho < R) wvT[((size_t)h * d + e) * R + rho] = tile[tx][k];
   }
+}
+
+template <int R>
+static hipError_t absorb_launch(const uint16_t* q, const uint16_t* wk, uint16_t* q_lat, int N, int H,
+                                int d, float qscale, hipStream_t st) {
+  const dim3 grid((N + 31) / 32, H);
+  switch (d) {
+    case 32: hipLaunchKernelGGL((absorb_bf16<R, 2>), grid, dim3(256), 0, st, q, wk, q_lat, N, H, qscale); break;
+    case 64: hipLaunchKernelGGL((absorb_bf16<R, 4>), grid, dim3(256), 0, st, q, wk, q_lat, N, H, qscale); break;
+    case 128: hipLaunchKernelGGL((absorb_bf16<R, 8>), grid, dim3(256), 0, st, q, wk, q_lat, N, H, qscale); break;
+    case 256: hipLaunchKernelGGL((absorb_bf16<R, 16>), grid, dim3(256), 0, st, q, wk, q_lat, N, H, qscale); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t absorb_mfma(const uint16_t* q, const uint16_t* wk, uint16_t* q_lat, int N, int H, int d,
+                       int R, float qscale, hipStream_t st) {
+  ProfScope ps("absorb_bf16", st);
+  switch (R) {
+    case 128: return absorb_launch<128>(q, wk, q_lat, N, H, d, qscale, st);
+    case 256: return absorb_launch<256>(q, wk, q_lat, N, H, d, qscale, st);
+    case 512: return absorb_launch<512>(q, wk, q_lat, N, H, d, qscale, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t transpose_wv_launch(const uint16_t* wv, uint16_t* wvT, int R, int H, int d, hipStream_t st) {
+  hipLaunchKernelGGL(transpose_wv, dim3((R + 31) / 32, (d + 31) / 32, H), dim3(256), 0, st, wv, wvT, R, H, d);
+  return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------
@@ -126,147 +153,6 @@ __global__ __launch_bounds__(256) void up_bf16(const uint16_t* __restrict__ o_la
                    pack_bf16x2(acc[i][4 * j + 2], acc[i][4 * j + 3])};
         *(u32x2*)(dst + e) = v;
       }
-}
-
-// ---------------------------------------------------------------------------
-// One wave's share of a latent tile of 32 keys (keys k0 .. k0+31 of the tile
-// held in LDS at `tile`, rows of R bf16, chunk-swizzled): scores, online
-// softmax update and the P * latent accumulation for the wave's 32 query
-// rows.  Lane l owns query row l%32 (lanes l and l^32 share it, each holding
-// half of its keys and half of its output columns).
-//   S^T[key][row]  = sum_rho L[key][rho] * q_lat[row][rho]        (A = L, B = q_lat^T)
-//   O^T[rho][row] += sum_key L[key][rho] * P[row][key]            (A = L^T, B = P^T)
-// The P^T operand is the softmax of the S^T accumulator as it sits in the
-// registers: key slot (g, u) of a 16-key step ks is key 16 ks + 8 (u/4) + 4 g + u%4,
-// and the L^T operand is read with LDS transpose reads in the same order.
-// Slack (log2 units) the running max may lag the true max before the
-// accumulators are rescaled; probabilities then stay <= 2^8.
-constexpr float kRescaleSlack = 8.f;
-
-template <int R>
-struct TileMath {
-  static constexpr int NKK = R / 16;  // 16-wide steps of the rho contraction
-  static constexpr int NOB = R / 32;  // 32-row blocks of the output columns
-
-  // key_limit: keys with absolute index > key_limit are masked (pass a huge
-  // value for tiles entirely inside every row's causal window).
-  static __device__ __forceinline__ void step(const char* tile, int k0, const bf16x8* qf,
-                                              f32x16* o, float& m_run, float& l_run,
-                                              int key_limit, bool need_mask, float sl2) {
-    const int lane = threadIdx.x & 63;
-    const int g = lane >> 5, l32 = lane & 31;
-    // ---- scores.  Chunk 2 kk + g of row l32 sits at 16 ((2 kk + g) ^ f) within
-    // its aligned group of 16 chunks: 8 per-lane offsets plus 256-byte steps.
-    f32x16 s;
-    {
-      const char* arow = tile + l32 * (R * 2);
-      const int f = swz(l32);
-#pragma unroll
-      for (int b = 0; b < 8; ++b) {
-        const char* p = arow + 16 * ((2 * b + g) ^ f);
-#pragma unroll
-        for (int a = 0; a < NKK / 8; ++a) {
-          const bf16x8 av = *(const bf16x8*)(p + 256 * a);
-          if (a == 0 && b == 0)
-            mfma32x32x16_v0(s, av, qf[0]);
-          else
-            mfma32x32x16_v(s, av, qf[8 * a + b]);
-        }
-      }
-      mfma_vgpr_drain(s);
-    }
-    // ---- online softmax (base-2 exponentials; sl2 = scale * log2 e).
-    // The reference max m_run only moves when a tile's max exceeds it by more
-    // than kRescaleSlack (then O and l are rescaled by 2^(m_old - m_new));
-    // otherwise probabilities up to 2^kRescaleSlack are accumulated against the
-    // older max.  The normalised result is the same; the rescale is rare.
-    float x[16];
-#pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      x[v] = s[v] * sl2;
-      if (need_mask) {
-        const int key = k0 + 8 * (v >> 2) + 4 * g + (v & 3);
-        if (key > key_limit) x[v] = -INFINITY;
-      }
-    }
-    float mt = x[0];
-#pragma unroll
-    for (int v = 1; v < 16; ++v) mt = fmaxf(mt, x[v]);
-    mt = fmaxf(mt, __shfl_xor(mt, 32));
-    // a row with no valid key in this tile has mt = -inf and never rescales
-    const bool grow = mt > m_run + kRescaleSlack;
-    if (__builtin_amdgcn_ballot_w64(grow)) {
-      const float alpha = grow ? exp2f(m_run - mt) : 1.f;
-      if (grow) m_run = mt;
-      l_run *= alpha;
-      mfma_agpr_wait();
-#pragma unroll
-      for (int c = 0; c < NOB; ++c) {  // one block at a time: 16 VGPR temporaries
-        mfma_agpr_tie(o[c]);
-        o[c] *= alpha;
-        mfma_agpr_tie(o[c]);
-      }
-    }
-    const float msub = m_run == -INFINITY ? 0.f : m_run;
-    bf16x8 P[2];
-    float ps = 0.f;
-#pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const float p = exp2f(x[v] - msub);
-      ps += p;
-      P[v >> 3][v & 7] = (__bf16)p;
-    }
-    l_run += ps;
-    // ---- O^T += L^T P^T.  Transpose reads of keys 16 ks + 4 g + m/4 (+8) and
-    // output columns rho = 32 c + 16 half + 4 (m%4): with the row swizzle the
-    // chunk offset is 16 (4 (c%4 ^ m/4) + (x ^ g)) (x ^ (g+2) for the +8 rows)
-    // within each 256-byte group, x = 2 half + (m%4)/2.
-    mfma_operand_ready(P[0]);
-    mfma_operand_ready(P[1]);
-    const int G = lane >> 4, m = lane & 15;
-    const int xo = 2 * (G & 1) + ((m & 3) >> 1);
-    const char* base = tile + (4 * g + (m >> 2)) * (R * 2) + 8 * (m & 1);
-#pragma unroll
-    for (int bq = 0; bq < 4; ++bq) {
-      const char* pa = base + 16 * (4 * (bq ^ (m >> 2)) + (xo ^ g));
-      const char* pb = base + 8 * (R * 2) + 16 * (4 * (bq ^ (m >> 2)) + (xo ^ (g + 2)));
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-        for (int aq = 0; aq < NOB / 4; ++aq) {
-          const int c = 4 * aq + bq;
-          const i16x4 lo = lds_read_tr16(pa + 16 * (R * 2) * ks + 256 * aq);
-          const i16x4 hi = lds_read_tr16(pb + 16 * (R * 2) * ks + 256 * aq);
-          const u32x2 lo2 = __builtin_bit_cast(u32x2, lo), hi2 = __builtin_bit_cast(u32x2, hi);
-          const u32x4 a4 = {lo2[0], lo2[1], hi2[0], hi2[1]};
-          mfma32x32x16_a(o[c], __builtin_bit_cast(bf16x8, a4), P[ks]);
-        }
-    }
-  }
-};
-
-// Copy keys k0 .. k0+31 of one batch's latents into a swizzled LDS tile with
-// LDS-DMA loads (global_load_lds_dwordx4: lane i of an instruction lands at
-// LDS base + 16 i, so the swizzle is applied by choosing the source chunk).
-// Keys past nkeys-1 read row nkeys-1 instead; the caller masks them.
-// The tile is 32 instructions of 1 KB; this thread's wave issues instructions
-// first, first + step, ...
-template <int R>
-__device__ __forceinline__ void dma_tile(const uint16_t* latb, int k0, int nkeys, char* tile,
-                                         int first, int step) {
-  constexpr int NC = R / 8;
-  constexpr int NINSTR = 32 * R * 2 / 1024;
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int k = first; k < NINSTR; k += step) {
-    const int idx = k * 64 + lane;
-    const int s = idx / NC, p = idx % NC;
-    const int c = (p & ~15) | ((p & 15) ^ swz(s));
-    const int key = k0 + s < nkeys ? k0 + s : nkeys - 1;
-    __builtin_amdgcn_global_load_lds(
-        (const __attribute__((address_space(1))) void*)(latb + (size_t)key * R + 8 * c),
-        (__attribute__((address_space(3))) void*)(uintptr_t)(tile + k * 1024), 16, 0, 0);
-  }
 }
 
 // ---------------------------------------------------------------------------
@@ -350,15 +236,6 @@ __device__ __forceinline__ void dma_tileT(const uint16_t* src, char* tbuf, int w
         (const __attribute__((address_space(1))) void*)((const char*)src + k * 1024 + 16 * lane),
         (__attribute__((address_space(3))) void*)(uintptr_t)(tbuf + k * 1024), 16, 0, 0);
   }
-}
-
-// Wait until at most n of this wave's vector-memory operations (here: the
-// LDS-DMA copies, in issue order) are still outstanding.
-template <int n>
-__device__ __forceinline__ void wait_vmem_outstanding() {
-  static_assert(n >= 0 && n < 64, "vmcnt range");
-  // s_waitcnt fields: vmcnt[3:0] and [15:14], expcnt[6:4], lgkmcnt[11:8]
-  __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
 // Per-wave tile math of the prefill kernel on 16x16x32 matrix instructions.
@@ -603,150 +480,6 @@ void flash_latent_bf16(const uint16_t* __restrict__ q_lat, const uint16_t* __res
 }
 
 // ---------------------------------------------------------------------------
-// Decode, split-K.  Block (split, head group, b): keys [split*CH, split*CH+CH)
-// of sequence b (CH = 4 waves x TPW tiles x 32 keys), query rows = 32 heads
-// of the group.  Wave w takes tiles w, w+4, ... of the chunk into its own LDS
-// tile; the four waves' softmax states are merged in LDS and the block writes
-// one partial state (m, l, unnormalised o_lat) per head.
-template <int R, int TPW>
-__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
-void decode_split_bf16(const uint16_t* __restrict__ q_lat, const uint16_t* __restrict__ lat,
-                       const int32_t* __restrict__ seq_lens, float* __restrict__ part_o,
-                       float* __restrict__ part_ml, int B, int Tmax, int H, int nsplit,
-                       float sl2) {
-  constexpr int TILE_BYTES = 32 * R * 2;
-  constexpr int CH = 4 * TPW * 32;
-  extern __shared__ __attribute__((aligned(16))) char dsmem[];
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int g = lane >> 5, l32 = lane & 31;
-  const int split = blockIdx.x, hg = blockIdx.y, b = blockIdx.z;
-  int L = seq_lens[b];
-  L = L < 1 ? 1 : (L > Tmax ? Tmax : L);
-  const int kbeg = split * CH;
-  if (kbeg >= L) return;  // whole block: this split holds no key
-  const int h = hg * 32 + l32;
-  const int hc = h < H ? h : H - 1;
-
-  bf16x8 qf[TileMath<R>::NKK];
-  {
-    const uint16_t* qrow = q_lat + ((size_t)b * H + hc) * R + 8 * g;
-#pragma unroll
-    for (int kk = 0; kk < TileMath<R>::NKK; ++kk) qf[kk] = *(const bf16x8*)(qrow + 16 * kk);
-  }
-  f32x16 o[TileMath<R>::NOB];
-#pragma unroll
-  for (int c = 0; c < TileMath<R>::NOB; ++c) o[c] = f32x16{};
-  float m_run = -INFINITY, l_run = 0.f;
-
-  char* tile = dsmem + w * TILE_BYTES;
-  const uint16_t* latb = lat + (size_t)b * Tmax * R;
-  const int kend = kbeg + CH < L ? kbeg + CH : L;
-  for (int j = w; j < TPW * 4; j += 4) {
-    const int k0 = kbeg + 32 * j;
-    if (k0 >= kend) break;
-    // wave-private tile, filled by this wave alone
-    dma_tile<R>(latb, k0, kend, tile, 0, 1);
-    wait_all_memory();
-    __builtin_amdgcn_wave_barrier();
-    TileMath<R>::step(tile, k0, qf, o, m_run, l_run, kend - 1, k0 + 31 >= kend, sl2);
-    __builtin_amdgcn_wave_barrier();
-  }
-  // ---- merge the four waves: 3 -> 1, 2 -> 0, then 1 -> 0 (LDS holds 2 states)
-  mfma_agpr_wait();
-#pragma unroll
-  for (int c = 0; c < TileMath<R>::NOB; ++c) mfma_agpr_tie(o[c]);
-  __syncthreads();
-  float* xo = (float*)dsmem;                       // [2][NOB*4][64] f32x4 (32 R floats per state)
-  float* xml = (float*)(dsmem + 2 * 32 * R * 4);   // [2][64][2]
-  auto put = [&](int slot) {
-    f32x4* dst = (f32x4*)(xo + (size_t)slot * 32 * R);
-#pragma unroll
-    for (int c = 0; c < TileMath<R>::NOB; ++c) {
-      mfma_agpr_tie(o[c]);
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        dst[(c * 4 + j) * 64 + lane] = f32x4{o[c][4 * j], o[c][4 * j + 1], o[c][4 * j + 2], o[c][4 * j + 3]};
-    }
-    xml[(slot * 64 + lane) * 2] = m_run;
-    xml[(slot * 64 + lane) * 2 + 1] = l_run;
-  };
-  auto take = [&](int slot) {
-    const f32x4* src = (const f32x4*)(xo + (size_t)slot * 32 * R);
-    const float mo = xml[(slot * 64 + lane) * 2], lo = xml[(slot * 64 + lane) * 2 + 1];
-    const float mn = fmaxf(m_run, mo);
-    if (mn == -INFINITY) return;  // neither state has seen a key
-    const float fa = exp2f(m_run - mn), fb = exp2f(mo - mn);
-#pragma unroll
-    for (int c = 0; c < TileMath<R>::NOB; ++c) {
-      mfma_agpr_tie(o[c]);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const f32x4 v = src[(c * 4 + j) * 64 + lane];
-        o[c][4 * j] = o[c][4 * j] * fa + v[0] * fb;
-        o[c][4 * j + 1] = o[c][4 * j + 1] * fa + v[1] * fb;
-        o[c][4 * j + 2] = o[c][4 * j + 2] * fa + v[2] * fb;
-        o[c][4 * j + 3] = o[c][4 * j + 3] * fa + v[3] * fb;
-      }
-      mfma_agpr_tie(o[c]);
-    }
-    l_run = l_run * fa + lo * fb;
-    m_run = mn;
-  };
-  if (w >= 2) put(w - 2);
-  __syncthreads();
-  if (w < 2) take(w);
-  __syncthreads();
-  if (w == 1) put(0);
-  __syncthreads();
-  if (w != 0) return;
-  take(0);
-  const float lt = l_run + __shfl_xor(l_run, 32);
-  if (h >= H) return;
-  const size_t prow = ((size_t)b * nsplit + split) * H + h;
-  float* po = part_o + prow * R;
-#pragma unroll
-  for (int c = 0; c < TileMath<R>::NOB; ++c)
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      *(f32x4*)(po + 32 * c + 8 * j + 4 * g) = f32x4{o[c][4 * j], o[c][4 * j + 1], o[c][4 * j + 2], o[c][4 * j + 3]};
-  if (g == 0) {
-    part_ml[prow * 2] = m_run;
-    part_ml[prow * 2 + 1] = lt;
-  }
-}
-
-// Log-sum-exp merge of the split states of one (b, h):
-//   m* = max_i m_i,  l* = sum_i l_i 2^(m_i - m*),  o = sum_i o_i 2^(m_i - m*) / l*.
-// Splits that saw no key (m = -inf) contribute nothing.  Writes o_lat [B*H][R] bf16.
-__global__ void decode_merge(const float* __restrict__ part_o, const float* __restrict__ part_ml,
-                             const int32_t* __restrict__ seq_lens, uint16_t* __restrict__ o_lat,
-                             int B, int Tmax, int H, int R, int nsplit, int chunk) {
-  const int bh = blockIdx.x;
-  const int b = bh / H, h = bh % H;
-  int L = seq_lens[b];
-  L = L < 1 ? 1 : (L > Tmax ? Tmax : L);
-  const int nact = (L + chunk - 1) / chunk;
-  float mstar = -INFINITY;
-  for (int i = 0; i < nact; ++i) mstar = fmaxf(mstar, part_ml[(((size_t)b * nsplit + i) * H + h) * 2]);
-  float lstar = 0.f;
-  for (int i = 0; i < nact; ++i) {
-    const size_t pr = ((size_t)b * nsplit + i) * H + h;
-    const float mi = part_ml[pr * 2];
-    if (mi != -INFINITY) lstar += part_ml[pr * 2 + 1] * exp2f(mi - mstar);
-  }
-  const float inv = 1.f / lstar;
-  for (int rho = threadIdx.x; rho < R; rho += blockDim.x) {
-    float acc = 0.f;
-    for (int i = 0; i < nact; ++i) {
-      const size_t pr = ((size_t)b * nsplit + i) * H + h;
-      const float mi = part_ml[pr * 2];
-      if (mi != -INFINITY) acc += part_o[pr * R + rho] * exp2f(mi - mstar);
-    }
-    o_lat[((size_t)b * H + h) * R + rho] = f32_to_bf16(acc * inv);
-  }
-}
-
-// ---------------------------------------------------------------------------
 // Host-side launchers (called by the C ABI after validation).
 template <int R>
 static hipError_t run_prefill(const uint16_t* q, const uint16_t* lat, const uint16_t* wk,
@@ -762,13 +495,12 @@ static hipError_t run_prefill(const uint16_t* q, const uint16_t* lat, const uint
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  {
-    ProfScope ps("absorb_bf16", st);
-    hipLaunchKernelGGL(absorb_bf16<R>, dim3((N + 31) / 32, H), dim3(256), 0, st, q, wk, q_lat, N, H, d, sl2);
-  }
+  hipError_t e = absorb_mfma(q, wk, q_lat, N, H, d, R, sl2, st);
+  if (e != hipSuccess) return e;
   {
     ProfScope ps("transpose_wv", st);
-    hipLaunchKernelGGL(transpose_wv, dim3((R + 31) / 32, (d + 31) / 32, H), dim3(256), 0, st, wv, wvT, R, H, d);
+    e = transpose_wv_launch(wv, wvT, R, H, d, st);
+    if (e != hipSuccess) return e;
   }
   {
     ProfScope ps("latent_transpose", st);
@@ -784,46 +516,6 @@ static hipError_t run_prefill(const uint16_t* q, const uint16_t* lat, const uint
   {
     ProfScope ps("up_bf16", st);
     hipLaunchKernelGGL(up_bf16<R>, dim3((N + 127) / 128, H), dim3(256), 0, st, o_lat, wvT, out, N, H, d);
-  }
-  return hipGetLastError();
-}
-
-template <int R>
-static hipError_t run_decode(const uint16_t* q, const uint16_t* lat, const int32_t* lens,
-                             const uint16_t* wk, const uint16_t* wv, uint16_t* out, int B,
-                             int Tmax, int H, int d, float sl2, uint16_t* q_lat, float* part_o,
-                             float* part_ml, uint16_t* o_lat, uint16_t* wvT, hipStream_t st) {
-  constexpr int TPW = kDecodeTilesPerWave;
-  constexpr int CH = 4 * TPW * 32;
-  const int nsplit = (Tmax + CH - 1) / CH;
-  const size_t lds = decode_lds_bytes(R);
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)decode_split_bf16<R, TPW>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
-  {
-    ProfScope ps("absorb_bf16", st);
-    hipLaunchKernelGGL(absorb_bf16<R>, dim3((B + 31) / 32, H), dim3(256), 0, st, q, wk, q_lat, B, H, d, 1.f);
-  }
-  {
-    ProfScope ps("transpose_wv", st);
-    hipLaunchKernelGGL(transpose_wv, dim3((R + 31) / 32, (d + 31) / 32, H), dim3(256), 0, st, wv, wvT, R, H, d);
-  }
-  {
-    ProfScope ps("decode_split_bf16", st);
-    hipLaunchKernelGGL((decode_split_bf16<R, TPW>), dim3(nsplit, (H + 31) / 32, B), dim3(256), lds, st,
-                       q_lat, lat, lens, part_o, part_ml, B, Tmax, H, nsplit, sl2);
-  }
-  {
-    ProfScope ps("decode_merge", st);
-    hipLaunchKernelGGL(decode_merge, dim3(B * H), dim3(256), 0, st, part_o, part_ml, lens, o_lat, B, Tmax, H, R, nsplit, CH);
-  }
-  {
-    ProfScope ps("up_bf16", st);
-    hipLaunchKernelGGL(up_bf16<R>, dim3((B + 127) / 128, H), dim3(256), 0, st, o_lat, wvT, out, B, H, d);
   }
   return hipGetLastError();
 }
@@ -850,44 +542,6 @@ size_t prefill_mfma_workspace(int B, int T, int H, int d, int r) {
   const size_t rows = (size_t)B * T * H;
   const size_t nt = ((size_t)T + 31) / 32;
   return (2 * rows * r + (size_t)H * d * r + (size_t)B * nt * 32 * r) * 2;
-}
-
-int decode_nsplit(int Tmax) {
-  constexpr int CH = 4 * kDecodeTilesPerWave * 32;
-  return (Tmax + CH - 1) / CH;
-}
-
-size_t decode_mfma_workspace(int B, int Tmax, int H, int d, int r) {
-  const size_t ns = decode_nsplit(Tmax);
-  size_t bytes = 0;
-  bytes += (size_t)B * H * r * 2;                   // q_lat
-  bytes += (size_t)B * H * r * 2;                   // o_lat
-  bytes += (size_t)H * d * r * 2;                   // W_uv^T
-  bytes = (bytes + 255) & ~(size_t)255;
-  bytes += (size_t)B * ns * H * r * 4;              // partial o
-  bytes += (size_t)B * ns * H * 2 * 4;              // partial (m, l)
-  return bytes;
-}
-
-hipError_t decode_mfma(const void* q, const void* lat, const int32_t* lens, const void* wk,
-                       const void* wv, void* out, int B, int Tmax, int H, int d, int r, float sl2,
-                       void* ws, hipStream_t st) {
-  const int ns = decode_nsplit(Tmax);
-  uint16_t* q_lat = (uint16_t*)ws;
-  uint16_t* o_lat = q_lat + (size_t)B * H * r;
-  uint16_t* wvT = o_lat + (size_t)B * H * r;
-  size_t off = ((size_t)B * H * r * 2 * 2 + (size_t)H * d * r * 2 + 255) & ~(size_t)255;
-  float* part_o = (float*)((char*)ws + off);
-  float* part_ml = part_o + (size_t)B * ns * H * r;
-#define ARGS (const uint16_t*)q, (const uint16_t*)lat, lens, (const uint16_t*)wk, \
-             (const uint16_t*)wv, (uint16_t*)out, B, Tmax, H, d, sl2, q_lat, part_o, part_ml, o_lat, wvT, st
-  switch (r) {
-    case 128: return run_decode<128>(ARGS);
-    case 256: return run_decode<256>(ARGS);
-    case 512: return run_decode<512>(ARGS);
-  }
-#undef ARGS
-  return hipErrorInvalidValue;
 }
 
 }  // namespace mla

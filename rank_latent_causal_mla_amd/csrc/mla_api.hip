@@ -180,6 +180,6 @@ mla_status mla_decode_fwd(const void* q, const void* kv_latent, const int32_t* s
 
 namespace mla {
 bool mfma_supported(int d, int r) {
-  return (r == 128 || r == 256 || r == 512) && d % 32 == 0 && d <= 256;
+  return (r == 128 || r == 256 || r == 512) && (d == 32 || d == 64 || d == 128 || d == 256);
 }
 }  // namespace mla

@@ -79,6 +79,18 @@ __device__ __forceinline__ float max_xor16(float v) {
 
 // LDS transpose read: within each group of 16 lanes, element k of lane i is
 // element i%4 of the 8 bytes addressed by lane 4k + i/4.
+// 2^x by the hardware exponential alone (no range reduction for results
+// below the smallest normal float, which flush to zero): softmax weights are
+// 2^(x - m) with x - m <= 8, where such results are negligible.
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// 16-byte read of LDS through an explicit LDS pointer: a generic pointer
+// whose address space the compiler cannot infer becomes a flat load, which
+// also waits on every outstanding global load.
+__device__ __forceinline__ bf16x8 lds_read16(const void* lds_byte_addr) {
+  return *(const __attribute__((address_space(3))) bf16x8*)(uintptr_t)lds_byte_addr;
+}
+
 __device__ __forceinline__ i16x4 lds_read_tr16(const void* lds_byte_addr) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)lds_byte_addr);
 }
@@ -102,6 +114,26 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 // Wait until every memory operation this wave issued has completed
 // (including LDS-DMA writes from global_load_lds).
 __device__ __forceinline__ void wait_all_memory() { __builtin_amdgcn_s_waitcnt(0); }
+
+// Wait until at most n of this wave's vector-memory operations (here: the
+// LDS-DMA copies, in issue order) are still outstanding.
+template <int n>
+__device__ __forceinline__ void wait_vmem_outstanding() {
+  static_assert(n >= 0 && n < 64, "vmcnt range");
+  // s_waitcnt fields: vmcnt[3:0] and [15:14], expcnt[6:4], lgkmcnt[11:8]
+  __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// XOR swizzle of 16-byte chunks inside a 16-chunk group of a row-major LDS
+// tile row s: f is a bijection on 0..15, so one chunk read from 16
+// consecutive rows hits 16 distinct 16-byte bank groups, and 4 consecutive
+// rows map an aligned chunk pair to 4 distinct pairs (transpose reads).
+__device__ __forceinline__ int swz(int s) { return ((s & 3) << 2) | ((s >> 2) & 3); }
+
+// Slack (log2 units) the online-softmax reference max may lag the running
+// max before the accumulators are rescaled; probabilities then stay <= 2^8.
+// The normalised result does not depend on it.
+constexpr float kRescaleSlack = 8.f;
 
 template <typename T> struct io;
 template <> struct io<float> {

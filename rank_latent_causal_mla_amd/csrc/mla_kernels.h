@@ -6,26 +6,32 @@
 
 namespace mla {
 
-// Decode split: each of the 4 waves of a block streams this many 32-key tiles.
-constexpr int kDecodeTilesPerWave = 8;
+// Decode: the ragged cache is cut into at most this many balanced splits
+// (plus at most one ragged end per sequence); workspace is sized for it.
+constexpr int decode_split_cap() { return 1024; }
+size_t decode_max_splits(int B);
 
-// LDS of the decode split kernel: four wave-private 32-key tiles, reused at
-// the end for two wave states plus their (m, l).
-constexpr size_t decode_lds_bytes(int R) { return (size_t)4 * 32 * R * 2 + 2 * 64 * 2 * 4; }
+// LDS of the decode split kernel: a ring of four 32-key latent tiles, the
+// probabilities of one tile (2 KB) and 64 row maxima.
+constexpr size_t decode_lds_bytes(int R) { return (size_t)4 * 32 * R * 2 + 2048 + 256; }
 
 // LDS of the prefill flash kernel: two row-major and three transposed 32-key tiles.
 constexpr size_t flash_lds_bytes(int R) { return (size_t)5 * 32 * R * 2; }
 
-// ---- bf16 matrix-core path (r in {128, 256, 512}, d % 32 == 0, d <= 256)
+// ---- bf16 matrix-core path (r in {128, 256, 512}, d in {32, 64, 128, 256})
 bool mfma_supported(int d, int r);
 hipError_t prefill_mfma(const void* q, const void* lat, const void* wk, const void* wv, void* out,
                         int B, int T, int H, int d, int r, float sl2, void* ws, hipStream_t st);
 size_t prefill_mfma_workspace(int B, int T, int H, int d, int r);
-int decode_nsplit(int Tmax);
 size_t decode_mfma_workspace(int B, int Tmax, int H, int d, int r);
 hipError_t decode_mfma(const void* q, const void* lat, const int32_t* lens, const void* wk,
                        const void* wv, void* out, int B, int Tmax, int H, int d, int r, float sl2,
                        void* ws, hipStream_t st);
+// q_lat[n*H + h, :] = qscale * W_uk[:, h, :] q[n, h, :] for N tokens (bf16).
+hipError_t absorb_mfma(const uint16_t* q, const uint16_t* wk, uint16_t* q_lat, int N, int H, int d,
+                       int R, float qscale, hipStream_t st);
+// W_uv [R, H, d] -> W_uv^T [H, d, R].
+hipError_t transpose_wv_launch(const uint16_t* wv, uint16_t* wvT, int R, int H, int d, hipStream_t st);
 
 // ---- SIMT path: float32 (or bf16 storage) with float32 arithmetic, any r <= 1024, d <= 256
 // dt_bf16: inputs and outputs stored as bf16 (else float32).
