@@ -5,73 +5,20 @@
 // sequence and attends keys 0..L_b-1): every head's r-wide query q_lat
 // attends the shared latents, the online softmax keeps (m, l, o_lat), and
 // o_lat is up-projected per head.  The cache is streamed once from HBM:
+//   decode_prep      -- split plan, absorption and W_uv transpose in one launch;
 //   decode_split     -- split-K over balanced chunks of every sequence; each
 //                       block writes one partial state per head;
 //   decode_merge_up  -- log-sum-exp merge of the partial states of each
 //                       (b, h), then the W_uv up-projection on the matrix unit.
 #include "mla_device.h"
 #include "mla_kernels.h"
+#include "prep_blocks.h"
 #include "profile.h"
 
 namespace mla {
 
 constexpr int kDecodeTileKeys = 32;  // keys per LDS tile of decode_split
 constexpr int kDecodeBufs = 4;       // tiles in its LDS ring
-
-// Balanced split of the ragged cache, computed on the device from the
-// device-resident lengths (one block): chunk C (a multiple of the 32-key
-// tile) is the smallest with sum_b ceil(L_b / C) <= target + B.  Sequence b
-// owns splits base_b .. base_b + cnt_b - 1; split s covers keys [k0, k1) of
-// sequence table[s].x (-1 past the last split).
-__device__ __forceinline__ int clamp_len(int L, int Tmax) { return L < 1 ? 1 : (L > Tmax ? Tmax : L); }
-
-__global__ __launch_bounds__(1024) void decode_plan(const int32_t* __restrict__ lens, int B, int Tmax,
-                                                    int target, int max_splits, int4* __restrict__ table,
-                                                    int2* __restrict__ seqinfo) {
-  __shared__ long long red[1024];
-  __shared__ int scan[1024];
-  __shared__ int carry;
-  const int tid = threadIdx.x;
-  long long part = 0;
-  for (int b = tid; b < B; b += 1024) part += clamp_len(lens[b], Tmax);
-  red[tid] = part;
-  __syncthreads();
-  for (int o = 512; o > 0; o >>= 1) {
-    if (tid < o) red[tid] += red[tid + o];
-    __syncthreads();
-  }
-  long long C = (red[0] + target - 1) / target;
-  C = (C + kDecodeTileKeys - 1) / kDecodeTileKeys * kDecodeTileKeys;
-  if (C < kDecodeTileKeys) C = kDecodeTileKeys;
-  if (tid == 0) carry = 0;
-  __syncthreads();
-  for (int b0 = 0; b0 < B; b0 += 1024) {
-    const int b = b0 + tid;
-    const int L = b < B ? clamp_len(lens[b], Tmax) : 0;
-    const int n = b < B ? (int)((L + C - 1) / C) : 0;
-    scan[tid] = n;
-    __syncthreads();
-    for (int o = 1; o < 1024; o <<= 1) {  // inclusive Hillis-Steele scan
-      const int v = tid >= o ? scan[tid - o] : 0;
-      __syncthreads();
-      scan[tid] += v;
-      __syncthreads();
-    }
-    const int base = carry + scan[tid] - n;
-    if (b < B) {
-      seqinfo[b] = int2{base, n};
-      for (int i = 0; i < n; ++i) {
-        const int k0 = (int)(i * C);
-        const int k1 = (int)((i + 1) * C) < L ? (int)((i + 1) * C) : L;
-        table[base + i] = int4{b, k0, k1, 0};
-      }
-    }
-    __syncthreads();
-    if (tid == 1023) carry += scan[1023];
-    __syncthreads();
-  }
-  for (int s2 = carry + tid; s2 < max_splits; s2 += 1024) table[s2] = int4{-1, 0, 0, 0};
-}
 
 // LDS-DMA copy of 16 bytes per lane (lane l: gptr -> LDS byte lds_base + 16 l).
 // Issued as inline assembly: the compiler then cannot pair every later LDS
@@ -322,86 +269,166 @@ void decode_split(const uint16_t* __restrict__ q_lat, const uint16_t* __restrict
   }
 }
 
+// Prologue of a decode call in one launch (independent block roles):
+//   block 0                  -- the split plan (table, seqinfo);
+//   the next nabs blocks     -- absorption, 32 sequences x 128 rho of one head each;
+//   the last ntr blocks      -- the W_uv transpose, 32 x 32 tiles.
+template <int R, int DK>
+__global__ __launch_bounds__(256) void decode_prep(const uint16_t* __restrict__ q, const uint16_t* __restrict__ wk,
+                                                   uint16_t* __restrict__ q_lat, const uint16_t* __restrict__ wv,
+                                                   uint16_t* __restrict__ wvT, const int32_t* __restrict__ lens,
+                                                   int B, int Tmax, int H, int d, float qscale, int target,
+                                                   int max_splits, int4* __restrict__ table,
+                                                   int2* __restrict__ seqinfo, int nabs) {
+  constexpr int NQ = R / 128;
+  const int bid = blockIdx.x;
+  if (bid == 0) {
+    plan_block(lens, B, Tmax, target, kDecodeTileKeys, max_splits, table, seqinfo);
+  } else if (bid <= nabs) {
+    const int t = bid - 1;
+    absorb_tile<R, DK, 1>(q, wk, q_lat, B, H, qscale, t / (H * NQ), (t / NQ) % H, 128 * (t % NQ));
+  } else {
+    const int t = bid - 1 - nabs;
+    const int nrb = R / 32, neb = (d + 31) / 32;
+    transpose_wv_tile(wv, wvT, R, H, d, t % nrb, (t / nrb) % neb, t / (nrb * neb));
+  }
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
 // Merge + up-projection.  Block (h, group of 16 sequences):
-//   o_b = sum_i w_i o_i / sum_i w_i,  w_i = l_i 2^(m_i - m*),  m* = max_i m_i
+//   o_b = sum_i w_i o_i,  w_i = l_i 2^(m_i - m*) / sum_k l_k 2^(m_k - m*),  m* = max_i m_i
 // over the splits i of sequence b (o_i normalised), then
 //   out[b, h, :] = o_b W_uv[:, h, :]   (16 x R times R x d on the matrix unit,
-//   W_uv^T [H][d][R] from transpose_wv).
+//   W_uv^T [H][d][R] from the prologue).
+// Wave w merges sequences 4 w .. 4 w + 3.  Every phase issues all its loads
+// before using them, so each costs about one memory round trip: the split
+// weights (lanes over splits), the weighted sum (lane 16 k + c owns rho
+// [c R / 16, (c + 1) R / 16) of sequence 4 w + k), the up-projection operands.
 template <int R>
 __global__ __launch_bounds__(256) void decode_merge_up(const uint16_t* __restrict__ part_o,
                                                        const float* __restrict__ part_ml,
                                                        const int2* __restrict__ seqinfo,
                                                        const uint16_t* __restrict__ wvT,
                                                        uint16_t* __restrict__ out, int B, int H, int d) {
+  constexpr int NCH = R / 128;  // 16-byte chunks per lane in the weighted sum
+  constexpr int NKS = R / 32;   // contraction steps of the up-projection
   __shared__ __attribute__((aligned(16))) uint16_t ob[16][R + 8];
-  __shared__ float mst[16], winv[16];
+  __shared__ float wts[4][4][64];  // [wave][sequence][split within a chunk of 64]
   const int h = blockIdx.x, b0 = blockIdx.y * 16;
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, w = tid >> 6;
-  // per-sequence max and weight sum: one lane group of 16 per sequence
-  if (tid < 256) {
-    const int i = tid >> 4, k = tid & 15;  // sequence b0 + i, splits k, k + 16, ...
-    const int b = b0 + i;
-    float mx = -INFINITY;
-    int2 si = int2{0, 0};
-    if (b < B) si = seqinfo[b];
-    for (int j = k; j < si.y; j += 16) mx = fmaxf(mx, part_ml[((size_t)(si.x + j) * H + h) * 2]);
-#pragma unroll
-    for (int o = 8; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
-    float ws = 0.f;
-    for (int j = k; j < si.y; j += 16) {
-      const size_t pr = (size_t)(si.x + j) * H + h;
-      ws += part_ml[pr * 2 + 1] * exp2f(part_ml[pr * 2] - mx);
-    }
-#pragma unroll
-    for (int o = 8; o > 0; o >>= 1) ws += __shfl_xor(ws, o);
-    if (k == 0) {
-      mst[i] = mx;
-      winv[i] = ws > 0.f ? 1.f / ws : 0.f;
-    }
-  }
-  __syncthreads();
-  // merged o_b (bf16) into LDS; thread t owns columns 2t, 2t+1 (R / 2 threads per sequence)
-  constexpr int TPS = R / 2;               // threads per sequence row
-  constexpr int SPP = 256 / TPS;           // sequences per pass
-  for (int i0 = 0; i0 < 16; i0 += SPP) {
-    const int i = i0 + tid / TPS, rho = 2 * (tid % TPS);
-    const int b = b0 + i;
-    float a0 = 0.f, a1 = 0.f;
-    if (b < B) {
-      const int2 si = seqinfo[b];
-      const float mx = mst[i];
-#pragma unroll 4
-      for (int j = 0; j < si.y; ++j) {
-        const size_t pr = (size_t)(si.x + j) * H + h;
-        const float wgt = part_ml[pr * 2 + 1] * exp2f(part_ml[pr * 2] - mx);
-        const uint32_t pv = *(const uint32_t*)(part_o + pr * R + rho);
-        a0 += wgt * bf16_to_f32((uint16_t)(pv & 0xFFFF));
-        a1 += wgt * bf16_to_f32((uint16_t)(pv >> 16));
-      }
-      a0 *= winv[i];
-      a1 *= winv[i];
-    }
-    *(uint32_t*)&ob[i][rho] = pack_bf16x2(a0, a1);
-  }
-  __syncthreads();
-  // out^T[e][b] = sum_rho W_uv^T[e][rho] o[b][rho]: A = W_uv^T (e rows), B = o^T
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int G = lane >> 4, n = lane & 15;
   const int neb = d / 16;
-  for (int eb = w; eb < neb; eb += 4) {
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    const uint16_t* wrow = wvT + ((size_t)h * d + 16 * eb + n) * R + 8 * G;
-#pragma unroll 4
-    for (int ks = 0; ks < R / 32; ++ks) {
-      const bf16x8 a = *(const bf16x8*)(wrow + 32 * ks);
-      const bf16x8 bo = *(const bf16x8*)&ob[n][32 * ks + 8 * G];
-      acc = mfma16x16x32(a, bo, acc);
+
+  // up-projection operands of this wave's first output block, in flight early
+  bf16x8 wa[NKS];
+  if (w < neb) {
+    const uint16_t* wrow = wvT + ((size_t)h * d + 16 * w + n) * R + 8 * G;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) wa[ks] = *(const bf16x8*)(wrow + 32 * ks);
+  }
+
+  int2 si[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int b = b0 + 4 * w + k;
+    si[k] = b < B ? seqinfo[b] : int2{0, 0};
+  }
+  // (m, l) of the first 64 splits of each sequence in registers, lane = split
+  float2 ml0[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+    ml0[k] = lane < si[k].y ? *(const float2*)(part_ml + ((size_t)(si[k].x + lane) * H + h) * 2)
+                            : float2{-INFINITY, 0.f};
+  float mx[4], inv[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    float m = ml0[k].x;
+    for (int j = lane + 64; j < si[k].y; j += 64) m = fmaxf(m, part_ml[((size_t)(si[k].x + j) * H + h) * 2]);
+    mx[k] = wave_max(m);
+  }
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    float ls = lane < si[k].y ? ml0[k].y * exp2f(ml0[k].x - mx[k]) : 0.f;
+    for (int j = lane + 64; j < si[k].y; j += 64) {
+      const float2 ml = *(const float2*)(part_ml + ((size_t)(si[k].x + j) * H + h) * 2);
+      ls += ml.y * exp2f(ml.x - mx[k]);
     }
-    // acc[v] = out^T[e = 16 eb + 4 G + v][b = b0 + n]
+    ls = wave_sum(ls);
+    inv[k] = ls > 0.f ? 1.f / ls : 0.f;
+  }
+
+  // weighted sum, in chunks of 64 splits
+  const int kq = G, c = n;
+  const int2 mys = b0 + 4 * w + kq < B ? seqinfo[b0 + 4 * w + kq] : int2{0, 0};
+  int maxc = si[0].y;
+#pragma unroll
+  for (int k = 1; k < 4; ++k) maxc = max(maxc, si[k].y);
+  float acc[8 * NCH];
+#pragma unroll
+  for (int i = 0; i < 8 * NCH; ++i) acc[i] = 0.f;
+  for (int c0 = 0; c0 < maxc; c0 += 64) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      float2 ml = ml0[k];
+      if (c0 > 0)
+        ml = c0 + lane < si[k].y ? *(const float2*)(part_ml + ((size_t)(si[k].x + c0 + lane) * H + h) * 2)
+                                 : float2{-INFINITY, 0.f};
+      wts[w][k][lane] = c0 + lane < si[k].y ? ml.y * exp2f(ml.x - mx[k]) * inv[k] : 0.f;
+    }
+    const int nj = min(64, maxc - c0);
+#pragma unroll 4
+    for (int jj = 0; jj < nj; ++jj) {
+      if (c0 + jj < mys.y) {
+        const float wt = wts[w][kq][jj];
+        const uint16_t* src = part_o + ((size_t)(mys.x + c0 + jj) * H + h) * R + c * (R / 16);
+#pragma unroll
+        for (int i = 0; i < NCH; ++i) {
+          const u32x4 v = *(const u32x4*)(src + 8 * i);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            acc[8 * i + 2 * e] += wt * __uint_as_float(v[e] << 16);
+            acc[8 * i + 2 * e + 1] += wt * __uint_as_float(v[e] & 0xFFFF0000u);
+          }
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < NCH; ++i) {
+    const u32x4 r = {pack_bf16x2(acc[8 * i], acc[8 * i + 1]), pack_bf16x2(acc[8 * i + 2], acc[8 * i + 3]),
+                     pack_bf16x2(acc[8 * i + 4], acc[8 * i + 5]), pack_bf16x2(acc[8 * i + 6], acc[8 * i + 7])};
+    *(u32x4*)&ob[4 * w + kq][c * (R / 16) + 8 * i] = r;
+  }
+  __syncthreads();
+
+  // out^T[e][b] = sum_rho W_uv^T[e][rho] o[b][rho]: A = W_uv^T (e rows), B = o^T
+  for (int eb = w; eb < neb; eb += 4) {
+    if (eb != w) {
+      const uint16_t* wrow = wvT + ((size_t)h * d + 16 * eb + n) * R + 8 * G;
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) wa[ks] = *(const bf16x8*)(wrow + 32 * ks);
+    }
+    f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < NKS; ks += 2) {
+      a0 = mfma16x16x32(wa[ks], *(const bf16x8*)&ob[n][32 * ks + 8 * G], a0);
+      a1 = mfma16x16x32(wa[ks + 1], *(const bf16x8*)&ob[n][32 * ks + 32 + 8 * G], a1);
+    }
+    // (a0 + a1)[v] = out^T[e = 16 eb + 4 G + v][b = b0 + n]
     const int b = b0 + n;
     if (b < B) {
       uint16_t* dst = out + ((size_t)b * H + h) * d + 16 * eb + 4 * G;
-      const u32x2 v = {pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])};
+      const u32x2 v = {pack_bf16x2(a0[0] + a1[0], a0[1] + a1[1]), pack_bf16x2(a0[2] + a1[2], a0[3] + a1[3])};
       *(u32x2*)dst = v;
     }
   }
@@ -439,15 +466,21 @@ static hipError_t run_decode(const uint16_t* q, const uint16_t* lat, const int32
     attr_set = true;
   }
   {
-    ProfScope ps("decode_plan", st);
-    hipLaunchKernelGGL(decode_plan, dim3(1), dim3(1024), 0, st, lens, B, Tmax, target, max_splits, table, seqinfo);
-  }
-  hipError_t e = absorb_mfma(q, wk, q_lat, B, H, d, R, sl2, st);
-  if (e != hipSuccess) return e;
-  {
-    ProfScope ps("transpose_wv", st);
-    e = transpose_wv_launch(wv, wvT, R, H, d, st);
-    if (e != hipSuccess) return e;
+    ProfScope ps("decode_prep", st);
+    const int nabs = ((B + 31) / 32) * H * (R / 128);
+    const int ntr = (R / 32) * ((d + 31) / 32) * H;
+    const dim3 grid(1 + nabs + ntr);
+#define PREP(DK)                                                                                          \
+  hipLaunchKernelGGL((decode_prep<R, DK>), grid, dim3(256), 0, st, q, wk, q_lat, wv, wvT, lens, B, Tmax, H, d, \
+                     sl2, target, max_splits, table, seqinfo, nabs)
+    switch (d) {
+      case 32: PREP(2); break;
+      case 64: PREP(4); break;
+      case 128: PREP(8); break;
+      case 256: PREP(16); break;
+      default: return hipErrorInvalidValue;
+    }
+#undef PREP
   }
   {
     ProfScope ps("decode_split", st);

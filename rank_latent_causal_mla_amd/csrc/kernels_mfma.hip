@@ -13,74 +13,25 @@
 // exp(m_old - m_new) whenever the max grows -- exact up to rounding.
 #include "mla_device.h"
 #include "mla_kernels.h"
+#include "prep_blocks.h"
 #include "profile.h"
 
 namespace mla {
 
 // ---------------------------------------------------------------------------
-// Absorption: q_lat[n*H + h, rho] = qscale * sum_e W_uk[rho, h, e] * q[n, h, e]
-// (n = b*T + t; qscale folds the softmax scale and log2 e into q_lat for the
-// flash kernel).  Computed transposed, q_lat^T = W_h q_h^T, so each lane ends
-// with 4 consecutive rho of one query row.  Block: 4 waves; wave w covers rho
-// in [w R/4, (w+1) R/4) for 32 tokens of one head.  DK = d / 16 steps of the
-// contraction, all operands of a step loaded before its matrix ops.
+// Absorption (one block per 32 query rows of one head, the whole rank) and
+// the W_uv transpose, as kernels around the block bodies of prep_blocks.h.
 template <int R, int DK>
 __global__ __launch_bounds__(256) void absorb_bf16(const uint16_t* __restrict__ q,
                                                    const uint16_t* __restrict__ wk,
                                                    uint16_t* __restrict__ q_lat, int N, int H,
                                                    float qscale) {
-  constexpr int NB = R / 128;  // 32-row blocks of rho per wave
-  constexpr int d = 16 * DK;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int g = lane >> 5, l32 = lane & 31;
-  const int h = blockIdx.y;
-  const int n = blockIdx.x * 32 + l32;
-  const int nc = min(n, N - 1);
-  const int rho0 = w * (R / 4);
-  const uint16_t* qrow = q + ((size_t)nc * H + h) * d + 8 * g;
-  bf16x8 bq[DK];
-#pragma unroll
-  for (int ks = 0; ks < DK; ++ks) bq[ks] = *(const bf16x8*)(qrow + 16 * ks);
-  f32x16 acc[NB];
-#pragma unroll
-  for (int i = 0; i < NB; ++i) {
-    const uint16_t* wrow = wk + ((size_t)(rho0 + 32 * i + l32) * H + h) * d + 8 * g;
-    bf16x8 a[DK];
-#pragma unroll
-    for (int ks = 0; ks < DK; ++ks) a[ks] = *(const bf16x8*)(wrow + 16 * ks);
-    acc[i] = f32x16{};
-#pragma unroll
-    for (int ks = 0; ks < DK; ++ks) acc[i] = mfma32x32x16(a[ks], bq[ks], acc[i]);
-  }
-  if (n >= N) return;
-  uint16_t* orow = q_lat + ((size_t)n * H + h) * R;
-#pragma unroll
-  for (int i = 0; i < NB; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int rho = rho0 + 32 * i + 8 * j + 4 * g;
-      u32x2 v = {pack_bf16x2(acc[i][4 * j] * qscale, acc[i][4 * j + 1] * qscale),
-                 pack_bf16x2(acc[i][4 * j + 2] * qscale, acc[i][4 * j + 3] * qscale)};
-      *(u32x2*)(orow + rho) = v;
-    }
+  absorb_tile<R, DK, R / 128>(q, wk, q_lat, N, H, qscale, blockIdx.x, blockIdx.y, 0);
 }
 
-// W_uv [R, H, d] -> W_uv^T [H, d, R], so the up-projection reads rho-contiguous rows.
-__global__ void transpose_wv(const uint16_t* __restrict__ wv, uint16_t* __restrict__ wvT, int R,
-                             int H, int d) {
-  __shared__ uint16_t tile[32][33];
-  const int h = blockIdx.z;
-  const int rho0 = blockIdx.x * 32, e0 = blockIdx.y * 32;
-  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;  // 32 x 8 threads
-  for (int k = ty; k < 32; k += 8) {
-    const int rho = rho0 + k, e = e0 + tx;
-    tile[k][tx] = (rho < R && e < d) ? wv[((size_t)rho * H + h) * d + e] : 0;
-  }
-  __syncthreads();
-  for (int k = ty; k < 32; k += 8) {
-    const int e = e0 + k, rho = rho0 + tx;
-    if (e < d && rho < R) wvT[((size_t)h * d + e) * R + rho] = tile[tx][k];
-  }
+__global__ __launch_bounds__(256) void transpose_wv(const uint16_t* __restrict__ wv, uint16_t* __restrict__ wvT,
+                                                    int R, int H, int d) {
+  transpose_wv_tile(wv, wvT, R, H, d, blockIdx.x, blockIdx.y, blockIdx.z);
 }
 
 template <int R>

@@ -1,0 +1,129 @@
+// Block bodies shared by the prefill kernels and the fused decode prologue:
+// weight absorption, the W_uv transpose and the decode split plan.  Each is
+// the work of one 256-thread block, given its block coordinates.
+#pragma once
+
+#include "mla_device.h"
+
+namespace mla {
+
+// Absorption: q_lat[n*H + h, rho] = qscale * sum_e W_uk[rho, h, e] * q[n, h, e]
+// (n = b*T + t; qscale folds the softmax scale and log2 e into q_lat).
+// Computed transposed, q_lat^T = W_h q_h^T, so each lane ends with 4
+// consecutive rho of one query row.  The block covers 32 query rows
+// (row block nb) of head h and the rank slice [rho_base, rho_base + 128 NB);
+// wave w takes 32 NB of those rho.  DK = d / 16 steps of the contraction,
+// all operands of a step loaded before its matrix ops.
+template <int R, int DK, int NB>
+__device__ __forceinline__ void absorb_tile(const uint16_t* __restrict__ q, const uint16_t* __restrict__ wk,
+                                            uint16_t* __restrict__ q_lat, int N, int H, float qscale, int nb,
+                                            int h, int rho_base) {
+  constexpr int d = 16 * DK;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int g = lane >> 5, l32 = lane & 31;
+  const int n = nb * 32 + l32;
+  const int nc = min(n, N - 1);
+  const int rho0 = rho_base + w * 32 * NB;
+  const uint16_t* qrow = q + ((size_t)nc * H + h) * d + 8 * g;
+  bf16x8 bq[DK];
+#pragma unroll
+  for (int ks = 0; ks < DK; ++ks) bq[ks] = *(const bf16x8*)(qrow + 16 * ks);
+  f32x16 acc[NB];
+#pragma unroll
+  for (int i = 0; i < NB; ++i) {
+    const uint16_t* wrow = wk + ((size_t)(rho0 + 32 * i + l32) * H + h) * d + 8 * g;
+    bf16x8 a[DK];
+#pragma unroll
+    for (int ks = 0; ks < DK; ++ks) a[ks] = *(const bf16x8*)(wrow + 16 * ks);
+    acc[i] = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < DK; ++ks) acc[i] = mfma32x32x16(a[ks], bq[ks], acc[i]);
+  }
+  if (n >= N) return;
+  uint16_t* orow = q_lat + ((size_t)n * H + h) * R;
+#pragma unroll
+  for (int i = 0; i < NB; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int rho = rho0 + 32 * i + 8 * j + 4 * g;
+      u32x2 v = {pack_bf16x2(acc[i][4 * j] * qscale, acc[i][4 * j + 1] * qscale),
+                 pack_bf16x2(acc[i][4 * j + 2] * qscale, acc[i][4 * j + 3] * qscale)};
+      *(u32x2*)(orow + rho) = v;
+    }
+}
+
+// W_uv [R, H, d] -> W_uv^T [H, d, R], so the up-projection reads rho-contiguous
+// rows.  The block transposes the 32 x 32 tile (rho block rb, e block eb) of head h.
+__device__ __forceinline__ void transpose_wv_tile(const uint16_t* __restrict__ wv, uint16_t* __restrict__ wvT,
+                                                  int R, int H, int d, int rb, int eb, int h) {
+  __shared__ uint16_t tile[32][33];
+  const int rho0 = rb * 32, e0 = eb * 32;
+  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;  // 32 x 8 threads
+  for (int k = ty; k < 32; k += 8) {
+    const int rho = rho0 + k, e = e0 + tx;
+    tile[k][tx] = (rho < R && e < d) ? wv[((size_t)rho * H + h) * d + e] : 0;
+  }
+  __syncthreads();
+  for (int k = ty; k < 32; k += 8) {
+    const int e = e0 + k, rho = rho0 + tx;
+    if (e < d && rho < R) wvT[((size_t)h * d + e) * R + rho] = tile[tx][k];
+  }
+}
+
+__device__ __forceinline__ int clamp_len(int L, int Tmax) { return L < 1 ? 1 : (L > Tmax ? Tmax : L); }
+
+// Decode split plan from the device-resident lengths (one 256-thread block).
+// Chunk C, a multiple of `align` keys, is the smallest with
+// sum_b ceil(L_b / C) <= target + B, for C = ceil(sum_b L_b / target) rounded
+// up to `align`.  Sequence b owns splits base_b .. base_b + cnt_b - 1
+// (seqinfo[b] = (base_b, cnt_b)); split s covers keys [k0, k1) of sequence
+// table[s].x, and table[s].x = -1 for every s past the last split, up to
+// max_splits.
+__device__ __forceinline__ void plan_block(const int32_t* __restrict__ lens, int B, int Tmax, int target,
+                                           int align, int max_splits, int4* __restrict__ table,
+                                           int2* __restrict__ seqinfo) {
+  __shared__ long long red[256];
+  __shared__ int scan[256];
+  __shared__ int carry;
+  const int tid = threadIdx.x;
+  long long part = 0;
+  for (int b = tid; b < B; b += 256) part += clamp_len(lens[b], Tmax);
+  red[tid] = part;
+  __syncthreads();
+  for (int o = 128; o > 0; o >>= 1) {
+    if (tid < o) red[tid] += red[tid + o];
+    __syncthreads();
+  }
+  long long C = (red[0] + target - 1) / target;
+  C = (C + align - 1) / align * align;
+  if (C < align) C = align;
+  if (tid == 0) carry = 0;
+  __syncthreads();
+  for (int b0 = 0; b0 < B; b0 += 256) {
+    const int b = b0 + tid;
+    const int L = b < B ? clamp_len(lens[b], Tmax) : 0;
+    const int n = b < B ? (int)((L + C - 1) / C) : 0;
+    scan[tid] = n;
+    __syncthreads();
+    for (int o = 1; o < 256; o <<= 1) {  // inclusive Hillis-Steele scan
+      const int v = tid >= o ? scan[tid - o] : 0;
+      __syncthreads();
+      scan[tid] += v;
+      __syncthreads();
+    }
+    const int base = carry + scan[tid] - n;
+    if (b < B) {
+      seqinfo[b] = int2{base, n};
+      for (int i = 0; i < n; ++i) {
+        const long long e = (i + 1) * C;
+        table[base + i] = int4{b, (int)(i * C), e < L ? (int)e : L, 0};
+      }
+    }
+    __syncthreads();
+    if (tid == 255) carry += scan[255];
+    __syncthreads();
+  }
+  for (int s = carry + tid; s < max_splits; s += 256) table[s] = int4{-1, 0, 0, 0};
+}
+
+}  // namespace mla
