@@ -66,21 +66,29 @@ __device__ __forceinline__ void dma_tile32(const uint16_t* latb, int k0, int ken
   }
 }
 
+// Wait until at most `later` tiles (NI copy instructions of this wave each)
+// are still in flight.
 template <int NI>
 __device__ __forceinline__ void dma_wait_tiles(int later) {
-  // at most `later` tiles (NI instructions each) of this wave still in flight
   switch (later) {
     case 0: dma_wait<0>(); break;
     case 1: dma_wait<NI>(); break;
-    case 2: dma_wait<2 * NI>(); break;
-    default: dma_wait<3 * NI>(); break;
+    default: dma_wait<2 * NI>(); break;
   }
 }
 
-// Split-K decode.  Block (split s, head group hg of 32 heads); the split is a
-// contiguous key range [k0, k1) of one sequence b, streamed through a ring of
-// kDecodeBufs block-shared LDS tiles of 32 keys.  The four waves share each
-// tile: wave w = 2 kb + qb computes the 16 x 16 score block of keys
+// Split-K decode over a balanced partition of the concatenated key space.
+// The keys of all sequences, one after another (sequence b owns positions
+// S[b] .. S[b+1]-1 of the exclusive prefix S of the clamped lengths), are
+// cut into P equal chunks of C = ceil(S[B] / P) keys; block (g, hg) takes
+// chunk g for head group hg (32 heads) and processes every sequence segment
+// in it, writing one partial state (normalised o, m, l) per segment into
+// slot g + b.  Every compute unit thus streams the same number of keys.
+//
+// A segment [k0, k1) of sequence b is streamed through a ring of
+// kDecodeBufs block-shared LDS tiles of 32 keys (three in flight while one is
+// read).  The four waves share each tile: wave
+// w = 2 kb + qb computes the 16 x 16 score block of keys
 // 16 kb .. 16 kb + 15 and heads 16 qb .. 16 qb + 15; the row maxima and the
 // probabilities P are exchanged through LDS; then wave w accumulates o_lat
 // for all 32 heads over its quarter of the latent columns.  Lane l = 16 G + n.
@@ -89,16 +97,21 @@ __device__ __forceinline__ void dma_wait_tiles(int later) {
 //            the tile's keys in the order 16 t + 4 G + v; A by two transpose reads)
 // Every wave tracks the running maxima of all 32 heads (identical in every
 // wave) and the partial sum l over its own 16 keys of its 16 heads.
+__device__ __forceinline__ int decode_chunk(int N, int P) {
+  const int C = (N + P - 1) / P;
+  return C < 1 ? 1 : C;
+}
+
 template <int R>
-__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
-void decode_split(const uint16_t* __restrict__ q_lat, const uint16_t* __restrict__ lat,
-                  const int4* __restrict__ table, uint16_t* __restrict__ part_o,
-                  float* __restrict__ part_ml, int Tmax, int H) {
+__device__ __forceinline__ void decode_segment(const uint16_t* __restrict__ q_lat,
+                                               const uint16_t* __restrict__ lat, uint16_t* __restrict__ part_o,
+                                               float* __restrict__ part_ml, int Tmax, int H, int hg, int b,
+                                               int k0, int k1, int slot) {
   constexpr int TILE = kDecodeTileKeys * R * 2;
-  constexpr int NI = TILE / 1024 / 4;
   constexpr int NKS = R / 32;       // contraction steps of a score block
   constexpr int NCW = R / 64;       // 16-column blocks of this wave's quarter
-  static_assert(kDecodeBufs - 2 <= 3, "dma_wait_tiles covers up to 3 later tiles");
+  constexpr int NI = TILE / 1024 / 4;  // copy instructions per wave and tile
+  static_assert(kDecodeBufs == 4, "dma_wait_tiles covers up to 2 later tiles");
   static_assert(NKS % 2 == 0, "two score chains");
   extern __shared__ __attribute__((aligned(16))) char smem[];
   // after the ring: P [2 q][4 G][16 n][2 kb][4] bf16, maxima [2 kb][2 q][16] f32
@@ -108,11 +121,6 @@ void decode_split(const uint16_t* __restrict__ q_lat, const uint16_t* __restrict
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int kb = w >> 1, qb = w & 1;
   const int G = lane >> 4, n = lane & 15;
-  const int s = blockIdx.x, hg = blockIdx.y;
-  const int4 sp = table[s];
-  const int b = __builtin_amdgcn_readfirstlane(sp.x);
-  if (b < 0) return;  // whole block: no split left
-  const int k0 = __builtin_amdgcn_readfirstlane(sp.y), k1 = __builtin_amdgcn_readfirstlane(sp.z);
   const int ntile = (k1 - k0 + kDecodeTileKeys - 1) / kDecodeTileKeys;
   const uint16_t* latb = lat + (size_t)b * Tmax * R;
   const uint32_t lds0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)smem);
@@ -253,7 +261,7 @@ void decode_split(const uint16_t* __restrict__ q_lat, const uint16_t* __restrict
     const int hh = hg * 32 + 16 * q + n;
     if (hh >= H) continue;
     const float inv = 1.f / lt;
-    const size_t prow = (size_t)s * H + hh;
+    const size_t prow = (size_t)slot * H + hh;
     uint16_t* po = part_o + prow * R + rw + 4 * G;
 #pragma unroll
     for (int c = 0; c < NCW; ++c) {
@@ -269,21 +277,49 @@ void decode_split(const uint16_t* __restrict__ q_lat, const uint16_t* __restrict
   }
 }
 
+template <int R>
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
+void decode_split(const uint16_t* __restrict__ q_lat, const uint16_t* __restrict__ lat,
+                  const int32_t* __restrict__ S, uint16_t* __restrict__ part_o,
+                  float* __restrict__ part_ml, int B, int Tmax, int H, int P) {
+  __shared__ int first_seq;
+  const int g = blockIdx.x, hg = blockIdx.y;
+  const int N = S[B];
+  const int C = decode_chunk(N, P);
+  int x0 = (int)min((long long)g * C, (long long)N);
+  const int x1 = (int)min((long long)x0 + C, (long long)N);
+  if (x0 >= x1) return;  // whole block: chunk past the end
+  // sequence holding key x0 (S is nondecreasing with positive steps)
+  for (int i = threadIdx.x; i < B; i += 256)
+    if (S[i] <= x0 && x0 < S[i + 1]) first_seq = i;
+  __syncthreads();
+  int b = __builtin_amdgcn_readfirstlane(first_seq);
+  for (;;) {
+    const int sb = __builtin_amdgcn_readfirstlane(S[b]);
+    const int se = __builtin_amdgcn_readfirstlane(S[b + 1]);
+    const int xe = x1 < se ? x1 : se;
+    decode_segment<R>(q_lat, lat, part_o, part_ml, Tmax, H, hg, b, x0 - sb, xe - sb, g + b);
+    x0 = xe;
+    if (x0 >= x1) break;
+    ++b;
+    __syncthreads();  // the ring and exchange buffers are free for the next segment
+  }
+}
+
 // Prologue of a decode call in one launch (independent block roles):
-//   block 0                  -- the split plan (table, seqinfo);
+//   block 0                  -- the prefix S of the clamped lengths;
 //   the next nabs blocks     -- absorption, 32 sequences x 128 rho of one head each;
 //   the last ntr blocks      -- the W_uv transpose, 32 x 32 tiles.
 template <int R, int DK>
 __global__ __launch_bounds__(256) void decode_prep(const uint16_t* __restrict__ q, const uint16_t* __restrict__ wk,
                                                    uint16_t* __restrict__ q_lat, const uint16_t* __restrict__ wv,
                                                    uint16_t* __restrict__ wvT, const int32_t* __restrict__ lens,
-                                                   int B, int Tmax, int H, int d, float qscale, int target,
-                                                   int max_splits, int4* __restrict__ table,
-                                                   int2* __restrict__ seqinfo, int nabs) {
+                                                   int B, int Tmax, int H, int d, float qscale,
+                                                   int32_t* __restrict__ S, int nabs) {
   constexpr int NQ = R / 128;
   const int bid = blockIdx.x;
   if (bid == 0) {
-    plan_block(lens, B, Tmax, target, kDecodeTileKeys, max_splits, table, seqinfo);
+    length_prefix_block(lens, B, Tmax, S);
   } else if (bid <= nabs) {
     const int t = bid - 1;
     absorb_tile<R, DK, 1>(q, wk, q_lat, B, H, qscale, t / (H * NQ), (t / NQ) % H, 128 * (t % NQ));
@@ -317,9 +353,9 @@ __device__ __forceinline__ float wave_sum(float v) {
 template <int R>
 __global__ __launch_bounds__(256) void decode_merge_up(const uint16_t* __restrict__ part_o,
                                                        const float* __restrict__ part_ml,
-                                                       const int2* __restrict__ seqinfo,
+                                                       const int32_t* __restrict__ S,
                                                        const uint16_t* __restrict__ wvT,
-                                                       uint16_t* __restrict__ out, int B, int H, int d) {
+                                                       uint16_t* __restrict__ out, int B, int H, int d, int P) {
   constexpr int NCH = R / 128;  // 16-byte chunks per lane in the weighted sum
   constexpr int NKS = R / 32;   // contraction steps of the up-projection
   __shared__ __attribute__((aligned(16))) uint16_t ob[16][R + 8];
@@ -337,12 +373,17 @@ __global__ __launch_bounds__(256) void decode_merge_up(const uint16_t* __restric
     for (int ks = 0; ks < NKS; ++ks) wa[ks] = *(const bf16x8*)(wrow + 32 * ks);
   }
 
+  // partial slots of sequence b: g + b for the chunks g that hold its keys
+  const int C = decode_chunk(S[B], P);
+  auto slots = [&](int b) {
+    if (b >= B) return int2{0, 0};
+    const int sb = S[b], se = S[b + 1];
+    const int g0 = sb / C, g1 = (se - 1) / C;
+    return int2{g0 + b, g1 - g0 + 1};
+  };
   int2 si[4];
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const int b = b0 + 4 * w + k;
-    si[k] = b < B ? seqinfo[b] : int2{0, 0};
-  }
+  for (int k = 0; k < 4; ++k) si[k] = slots(b0 + 4 * w + k);
   // (m, l) of the first 64 splits of each sequence in registers, lane = split
   float2 ml0[4];
 #pragma unroll
@@ -369,7 +410,7 @@ __global__ __launch_bounds__(256) void decode_merge_up(const uint16_t* __restric
 
   // weighted sum, in chunks of 64 splits
   const int kq = G, c = n;
-  const int2 mys = b0 + 4 * w + kq < B ? seqinfo[b0 + 4 * w + kq] : int2{0, 0};
+  const int2 mys = slots(b0 + 4 * w + kq);
   int maxc = si[0].y;
 #pragma unroll
   for (int k = 1; k < 4; ++k) maxc = max(maxc, si[k].y);
@@ -435,8 +476,7 @@ __global__ __launch_bounds__(256) void decode_merge_up(const uint16_t* __restric
 }
 
 // ---------------------------------------------------------------------------
-// Splits are sized so that about two blocks land on every compute unit.
-static int decode_target(int B) {
+static int device_cus() {
   static int cus = 0;
   if (cus == 0) {
     int dev = 0;
@@ -444,8 +484,7 @@ static int decode_target(int B) {
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
       cus = 256;
   }
-  const int t = 2 * cus - B;
-  return t > cus ? t : cus;
+  return cus;
 }
 
 size_t decode_max_splits(int B) { return (size_t)decode_split_cap() + B; }
@@ -454,9 +493,11 @@ template <int R>
 static hipError_t run_decode(const uint16_t* q, const uint16_t* lat, const int32_t* lens,
                              const uint16_t* wk, const uint16_t* wv, uint16_t* out, int B, int Tmax,
                              int H, int d, float sl2, uint16_t* q_lat, uint16_t* part_o, float* part_ml,
-                             uint16_t* wvT, int4* table, int2* seqinfo, hipStream_t st) {
-  const int target = decode_target(B) < decode_split_cap() ? decode_target(B) : decode_split_cap();
-  const int max_splits = target + B;
+                             uint16_t* wvT, int32_t* S, hipStream_t st) {
+  // one chunk of keys per compute unit over all head groups
+  const int nhg = (H + 31) / 32;
+  int P = device_cus() / nhg;
+  P = P < 1 ? 1 : (P > decode_split_cap() ? decode_split_cap() : P);
   const size_t lds = decode_lds_bytes(R);
   static bool attr_set = false;
   if (!attr_set) {
@@ -472,7 +513,7 @@ static hipError_t run_decode(const uint16_t* q, const uint16_t* lat, const int32
     const dim3 grid(1 + nabs + ntr);
 #define PREP(DK)                                                                                          \
   hipLaunchKernelGGL((decode_prep<R, DK>), grid, dim3(256), 0, st, q, wk, q_lat, wv, wvT, lens, B, Tmax, H, d, \
-                     sl2, target, max_splits, table, seqinfo, nabs)
+                     sl2, S, nabs)
     switch (d) {
       case 32: PREP(2); break;
       case 64: PREP(4); break;
@@ -484,52 +525,49 @@ static hipError_t run_decode(const uint16_t* q, const uint16_t* lat, const int32
   }
   {
     ProfScope ps("decode_split", st);
-    hipLaunchKernelGGL(decode_split<R>, dim3(max_splits, (H + 31) / 32), dim3(256), lds, st, q_lat, lat, table,
-                       part_o, part_ml, Tmax, H);
+    hipLaunchKernelGGL(decode_split<R>, dim3(P, nhg), dim3(256), lds, st, q_lat, lat, S, part_o, part_ml, B, Tmax,
+                       H, P);
   }
   {
     ProfScope ps("decode_merge_up", st);
-    hipLaunchKernelGGL(decode_merge_up<R>, dim3(H, (B + 15) / 16), dim3(256), 0, st, part_o, part_ml, seqinfo,
-                       wvT, out, B, H, d);
+    hipLaunchKernelGGL(decode_merge_up<R>, dim3(H, (B + 15) / 16), dim3(256), 0, st, part_o, part_ml, S, wvT, out,
+                       B, H, d, P);
   }
   return hipGetLastError();
 }
 
-// Workspace: q_lat [B*H][r] bf16 | W_uv^T [H][d][r] | partial o [S][H][r] bf16 |
-// partial (m, l) [S][H][2] f32 | split table [S] int4 | per-sequence (base, count) [B] int2,
-// with S = decode_split_cap() + B; each part 256-byte aligned.
+// Workspace: q_lat [B*H][r] bf16 | W_uv^T [H][d][r] | partial o [M][H][r] bf16 |
+// partial (m, l) [M][H][2] f32 | length prefix [B + 1] int32, with
+// M = decode_split_cap() + B partial slots; each part 256-byte aligned.
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 size_t decode_mfma_workspace(int B, int Tmax, int H, int d, int r) {
   (void)Tmax;
-  const size_t S = decode_max_splits(B);
+  const size_t M = decode_max_splits(B);
   size_t bytes = align256((size_t)B * H * r * 2);
   bytes = align256(bytes + (size_t)H * d * r * 2);
-  bytes = align256(bytes + S * H * r * 2);
-  bytes = align256(bytes + S * H * 2 * 4);
-  bytes = align256(bytes + S * 16);
-  bytes += (size_t)B * 8;
+  bytes = align256(bytes + M * H * r * 2);
+  bytes = align256(bytes + M * H * 2 * 4);
+  bytes += (size_t)(B + 1) * 4;
   return bytes;
 }
 
 hipError_t decode_mfma(const void* q, const void* lat, const int32_t* lens, const void* wk,
                        const void* wv, void* out, int B, int Tmax, int H, int d, int r, float sl2,
                        void* ws, hipStream_t st) {
-  const size_t S = decode_max_splits(B);
+  const size_t M = decode_max_splits(B);
   char* p = (char*)ws;
   uint16_t* q_lat = (uint16_t*)p;
   size_t off = align256((size_t)B * H * r * 2);
   uint16_t* wvT = (uint16_t*)(p + off);
   off = align256(off + (size_t)H * d * r * 2);
   uint16_t* part_o = (uint16_t*)(p + off);
-  off = align256(off + S * H * r * 2);
+  off = align256(off + M * H * r * 2);
   float* part_ml = (float*)(p + off);
-  off = align256(off + S * H * 2 * 4);
-  int4* table = (int4*)(p + off);
-  off = align256(off + S * 16);
-  int2* seqinfo = (int2*)(p + off);
+  off = align256(off + M * H * 2 * 4);
+  int32_t* S = (int32_t*)(p + off);
 #define ARGS (const uint16_t*)q, (const uint16_t*)lat, lens, (const uint16_t*)wk, (const uint16_t*)wv, \
-             (uint16_t*)out, B, Tmax, H, d, sl2, q_lat, part_o, part_ml, wvT, table, seqinfo, st
+             (uint16_t*)out, B, Tmax, H, d, sl2, q_lat, part_o, part_ml, wvT, S, st
   switch (r) {
     case 128: return run_decode<128>(ARGS);
     case 256: return run_decode<256>(ARGS);

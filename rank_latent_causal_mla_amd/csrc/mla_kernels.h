@@ -6,8 +6,9 @@
 
 namespace mla {
 
-// Decode: the ragged cache is cut into at most this many balanced splits
-// (plus at most one ragged end per sequence); workspace is sized for it.
+// Decode: at most this many equal chunks of the concatenated cache per head
+// group; a chunk holds one partial state per sequence segment, so a call
+// has at most decode_split_cap() + B - 1 partial slots (workspace sized for it).
 constexpr int decode_split_cap() { return 1024; }
 size_t decode_max_splits(int B);
 

@@ -1,5 +1,5 @@
 // Block bodies shared by the prefill kernels and the fused decode prologue:
-// weight absorption, the W_uv transpose and the decode split plan.  Each is
+// weight absorption, the W_uv transpose and the prefix of the decode lengths.  Each is
 // the work of one 256-thread block, given its block coordinates.
 #pragma once
 
@@ -72,38 +72,19 @@ __device__ __forceinline__ void transpose_wv_tile(const uint16_t* __restrict__ w
 
 __device__ __forceinline__ int clamp_len(int L, int Tmax) { return L < 1 ? 1 : (L > Tmax ? Tmax : L); }
 
-// Decode split plan from the device-resident lengths (one 256-thread block).
-// Chunk C, a multiple of `align` keys, is the smallest with
-// sum_b ceil(L_b / C) <= target + B, for C = ceil(sum_b L_b / target) rounded
-// up to `align`.  Sequence b owns splits base_b .. base_b + cnt_b - 1
-// (seqinfo[b] = (base_b, cnt_b)); split s covers keys [k0, k1) of sequence
-// table[s].x, and table[s].x = -1 for every s past the last split, up to
-// max_splits.
-__device__ __forceinline__ void plan_block(const int32_t* __restrict__ lens, int B, int Tmax, int target,
-                                           int align, int max_splits, int4* __restrict__ table,
-                                           int2* __restrict__ seqinfo) {
-  __shared__ long long red[256];
+// Exclusive prefix of the clamped decode lengths (one 256-thread block):
+// S[b] = sum_{b' < b} clamp(L_b'), S[B] = the total.
+__device__ __forceinline__ void length_prefix_block(const int32_t* __restrict__ lens, int B, int Tmax,
+                                                    int32_t* __restrict__ S) {
   __shared__ int scan[256];
   __shared__ int carry;
   const int tid = threadIdx.x;
-  long long part = 0;
-  for (int b = tid; b < B; b += 256) part += clamp_len(lens[b], Tmax);
-  red[tid] = part;
-  __syncthreads();
-  for (int o = 128; o > 0; o >>= 1) {
-    if (tid < o) red[tid] += red[tid + o];
-    __syncthreads();
-  }
-  long long C = (red[0] + target - 1) / target;
-  C = (C + align - 1) / align * align;
-  if (C < align) C = align;
   if (tid == 0) carry = 0;
   __syncthreads();
   for (int b0 = 0; b0 < B; b0 += 256) {
     const int b = b0 + tid;
     const int L = b < B ? clamp_len(lens[b], Tmax) : 0;
-    const int n = b < B ? (int)((L + C - 1) / C) : 0;
-    scan[tid] = n;
+    scan[tid] = L;
     __syncthreads();
     for (int o = 1; o < 256; o <<= 1) {  // inclusive Hillis-Steele scan
       const int v = tid >= o ? scan[tid - o] : 0;
@@ -111,19 +92,12 @@ __device__ __forceinline__ void plan_block(const int32_t* __restrict__ lens, int
       scan[tid] += v;
       __syncthreads();
     }
-    const int base = carry + scan[tid] - n;
-    if (b < B) {
-      seqinfo[b] = int2{base, n};
-      for (int i = 0; i < n; ++i) {
-        const long long e = (i + 1) * C;
-        table[base + i] = int4{b, (int)(i * C), e < L ? (int)e : L, 0};
-      }
-    }
+    if (b < B) S[b] = carry + scan[tid] - L;
     __syncthreads();
     if (tid == 255) carry += scan[255];
     __syncthreads();
   }
-  for (int s = carry + tid; s < max_splits; s += 256) table[s] = int4{-1, 0, 0, 0};
+  if (tid == 0) S[B] = carry;
 }
 
 }  // namespace mla
