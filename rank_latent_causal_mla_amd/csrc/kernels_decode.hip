@@ -12,59 +12,14 @@
 //                       (b, h), then the W_uv up-projection on the matrix unit.
 #include "mla_device.h"
 #include "mla_kernels.h"
+#include "lds_tiles.h"
 #include "prep_blocks.h"
 #include "profile.h"
 
 namespace mla {
 
-constexpr int kDecodeTileKeys = 32;  // keys per LDS tile of decode_split
+constexpr int kDecodeTileKeys = kTileKeys;  // keys per LDS tile of decode_split
 constexpr int kDecodeBufs = 4;       // tiles in its LDS ring
-
-// LDS-DMA copy of 16 bytes per lane (lane l: gptr -> LDS byte lds_base + 16 l).
-// Issued as inline assembly: the compiler then cannot pair every later LDS
-// transpose read with a wait for all copies in flight (it cannot tell which
-// LDS bytes a copy writes), which would serialise the prefetch.  The kernel
-// orders copies and reads itself with dma_wait<n>().
-__device__ __forceinline__ void dma16(const void* gptr, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-               :
-               : "v"(gptr), "s"(lds_base)
-               : "memory", "m0");
-}
-// Wait until at most n of this wave's vector-memory operations are outstanding.
-template <int n>
-__device__ __forceinline__ void dma_wait() {
-  static_assert(n >= 0 && n < 64, "vmcnt range");
-  asm volatile("s_waitcnt vmcnt(%0)" : : "n"(n) : "memory");
-}
-
-// Block-shared tile of 32 keys, row-major, 16-byte chunks XOR-swizzled by
-// tswz(key) inside every 16-chunk group:
-//   - score reads (16 lanes = 16 consecutive keys, one chunk each) hit 16
-//     distinct slots because tswz is a permutation of 0..15 on key % 16;
-//   - transpose reads (32 lanes = 8 consecutive keys x one chunk pair) hit 16
-//     distinct slots because tswz(key) >> 1 is a permutation of key % 8.
-__device__ __forceinline__ int tswz(int key) { return ((key & 7) << 1) | ((key >> 3) & 1); }
-
-// Wave w's share of the LDS-DMA copy of one tile: instructions i = w, w + 4, ...
-// of the tile's 32 R * 2 / 1024, each 64 lanes x 16 bytes.  The swizzle is
-// applied on the global side: LDS-DMA writes lane l to byte 16 l of its
-// 1 KB destination, so lane l fetches the chunk that belongs there.
-template <int R>
-__device__ __forceinline__ void dma_tile32(const uint16_t* latb, int k0, int kend, uint32_t tile, int w) {
-  constexpr int NC = R / 8;                                   // chunks per key row
-  constexpr int NI = kDecodeTileKeys * R * 2 / 1024 / 4;      // instructions per wave
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int i = 0; i < NI; ++i) {
-    const int ins = 4 * i + w;
-    const int idx = ins * 64 + lane;
-    const int s = idx / NC, p = idx % NC;
-    const int c = (p & ~15) | ((p & 15) ^ tswz(s));
-    const int key = k0 + s < kend ? k0 + s : kend - 1;
-    dma16(latb + (size_t)key * R + 8 * c, tile + ins * 1024);
-  }
-}
 
 // Wait until at most `later` tiles (NI copy instructions of this wave each)
 // are still in flight.

@@ -13,6 +13,7 @@
 // exp(m_old - m_new) whenever the max grows -- exact up to rounding.
 #include "mla_device.h"
 #include "mla_kernels.h"
+#include "lds_tiles.h"
 #include "prep_blocks.h"
 #include "profile.h"
 
@@ -109,138 +110,66 @@ __global__ __launch_bounds__(256) void up_bf16(const uint16_t* __restrict__ o_la
 // ---------------------------------------------------------------------------
 // Causal latent flash attention, prefill.
 //
-// The two products need the latent tile in two orientations: the scores
-// contract over rho (rows of L, rho-contiguous) and P * L contracts over keys
-// (columns of L).  Transposing in LDS (ds_read_b64_tr_b16) is far slower than
-// plain 16-byte reads, so the tile also comes pre-transposed from a per-call
-// copy of the latents, latT [B][ceil(T/32)][R][32] (latent_transpose below),
-// whose 32 keys per row are stored in the order the P operand holds them.
-// Both orientations are copied into LDS by LDS-DMA and read with ds_read_b128.
+// One block = 128 consecutive (t, h) rows of one batch; all its rows attend
+// the same latent tiles (K = V = latent), streamed through a ring of
+// kFlashBufs swizzled row-major 32-key tiles (lds_tiles.h) by LDS-DMA.  The
+// two products split the work differently over the four waves:
+//   scores + softmax: wave w owns rows 32 w .. 32 w + 31 (q_lat in registers);
+//   P * latent:       wave w owns latent columns [R w / 4, R (w + 1) / 4) of
+//                     all 128 rows (the output accumulator, in AGPRs).
+// Each tile's probabilities (bf16) and rescale factors go through LDS from
+// the row owners to the column owners.  Compared with one wave doing both
+// products for its own rows, every latent byte read from LDS by the second
+// product now serves 128 rows instead of 32, and the transposed operand is
+// read straight from the row tile with transpose reads, so each tile is
+// copied once.  Lane l = 16 G + n.
+//   scores:  S^T[16 kb + 4 G + v][16 qb + n] in s[kb][qb][v]     (16x16x32, A = L rows)
+//   P:       lane keeps, per own row block qb, the 8 probabilities of keys
+//            {16 kb + 4 G + v} = the P^T operand of that row block
+//   output:  O^T[R w / 4 + 16 c + 4 G + v][16 q + n] in o[c][q][v], q = 0..7 (A by TileCols)
+constexpr int kFlashBufs = 4;
 
-// Transposed tiles.  The P operand built from the score accumulators gives
-// lane group G (lanes 16 G .. 16 G + 15) the keys {4 G + u, 16 + 4 G + u},
-// u = 0..3, as its 8 k-slots.  The transposed copy of a 32-key tile is
-// therefore stored group-major, [G][rho][8]: entry u of (G, rho) holds
-// latent[key(G, u)][rho] with key(G, u) = 16 (u / 4) + 4 G + u % 4, so each
-// lane reads its A operand as one contiguous 16-byte chunk and the 16 lanes
-// of a group read 256 contiguous bytes.
-__device__ __forceinline__ int tkey(int G, int u) { return 16 * (u >> 2) + 4 * G + (u & 3); }
-
-// lat [B][T][R] -> latT [B][nt][4][R][8], nt = ceil(T / 32); keys >= T are zero.
-template <int R>
-__global__ __launch_bounds__(256) void latent_transpose(const uint16_t* __restrict__ lat,
-                                                        uint16_t* __restrict__ latT, int T, int nt) {
-  __shared__ __attribute__((aligned(16))) uint16_t s[32][R + 8];
-  const int tile = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
-  constexpr int NC = R / 8;
-  const uint16_t* src = lat + ((size_t)b * T + 32 * tile) * R;
-  for (int idx = tid; idx < 32 * NC; idx += 256) {
-    const int key = idx / NC, c = idx % NC;
-    const u32x4 v = 32 * tile + key < T ? *(const u32x4*)(src + (size_t)key * R + 8 * c) : u32x4{0, 0, 0, 0};
-    *(u32x4*)&s[key][8 * c] = v;
-  }
-  __syncthreads();
-  uint16_t* dst = latT + ((size_t)b * nt + tile) * R * 32;
-  for (int idx = tid; idx < 4 * R; idx += 256) {
-    const int G = idx / R, rho = idx % R;
-    uint32_t w[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      w[i] = (uint32_t)s[tkey(G, 2 * i)][rho] | ((uint32_t)s[tkey(G, 2 * i + 1)][rho] << 16);
-    *(u32x4*)(dst + (size_t)idx * 8) = u32x4{w[0], w[1], w[2], w[3]};
-  }
-}
-
-// Row-major LDS tile for the scores: key row s keeps 16-byte chunk c at
-// position c ^ (s & 15) within its aligned group of 16, so the reads of one
-// chunk by 16 consecutive key rows (one pass of a 16-byte LDS read) hit 16
-// distinct 16-byte bank groups.  The copy is 32 * R * 2 / 1024 LDS-DMA
-// instructions of 1 KB (lane i lands at base + 16 i); wave w (wave-uniform)
-// issues instructions w, w + 4, ...  Keys past nkeys-1 re-read row nkeys-1.
-template <int R>
-__device__ __forceinline__ void dma_rowtile(const uint16_t* latb, int k0, int nkeys, char* tile, int w) {
-  constexpr int NC = R / 8;
-  constexpr int NINSTR = 32 * R * 2 / 1024;
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int i = 0; i < NINSTR / 4; ++i) {
-    const int k = 4 * i + w;
-    const int idx = k * 64 + lane;
-    const int s = idx / NC, p = idx % NC;
-    const int c = (p & ~15) | ((p & 15) ^ (s & 15));
-    const int key = k0 + s < nkeys ? k0 + s : nkeys - 1;
-    __builtin_amdgcn_global_load_lds(
-        (const __attribute__((address_space(1))) void*)(latb + (size_t)key * R + 8 * c),
-        (__attribute__((address_space(3))) void*)(uintptr_t)(tile + k * 1024), 16, 0, 0);
-  }
-}
-
-// Transposed tile: a straight copy of its [4][R][8] image (R * 64 bytes).
-template <int R>
-__device__ __forceinline__ void dma_tileT(const uint16_t* src, char* tbuf, int w) {
-  constexpr int NINSTR = R * 64 / 1024;
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int i = 0; i < NINSTR / 4; ++i) {
-    const int k = 4 * i + w;
-    __builtin_amdgcn_global_load_lds(
-        (const __attribute__((address_space(1))) void*)((const char*)src + k * 1024 + 16 * lane),
-        (__attribute__((address_space(3))) void*)(uintptr_t)(tbuf + k * 1024), 16, 0, 0);
-  }
-}
-
-// Per-wave tile math of the prefill kernel on 16x16x32 matrix instructions.
-// Lane l = 16 G + n.  The wave's 32 query rows form two blocks qb (rows
-// 16 qb + n); a 32-key tile forms two key blocks kb.
-//   scores:  S^T[16 kb + 4 G + v][16 qb + n] in s[kb][qb][v]   (A = L rows, B = q_lat^T)
-//   P:       lane keeps, per qb, the 8 probabilities of its keys
-//            {16 kb + 4 G + v}: k-slot 8 G + 4 kb + v of the P^T operand.
-//   output:  O^T[16 c + 4 G + v][16 qb + n] in o[c][qb][v]      (A = L^T, B = P^T)
-// so each lane holds two query rows, and a row's keys sit in the four lanes
-// n + 16 G'.
 template <int R>
 struct Flash {
   static constexpr int NKS = R / 32;  // 32-wide steps of the rho contraction
-  static constexpr int NOB = R / 16;  // 16-row blocks of output columns
+  static constexpr int NCW = R / 64;  // 16-column blocks of a wave's quarter
+  static constexpr int NQ = 8;        // 16-row blocks of the block's rows
 
-  // Four independent accumulator chains keep the matrix unit busy.
-  static __device__ __forceinline__ void scores(const char* rowtile, const bf16x8 (*qf)[NKS],
-                                                f32x4 (&s)[2][2]) {
+  // S^T for the wave's 32 rows: four independent accumulator chains.
+  static __device__ __forceinline__ void scores(const char* tile, const bf16x8 (*qf)[NKS], f32x4 (&s)[2][2]) {
     const int lane = threadIdx.x & 63;
     const int G = lane >> 4, n = lane & 15;
+    const int f = tswz(n);  // rows n and 16 + n share the swizzle
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) s[kb][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
-    // read i = 2 ks + kb: key row 16 kb + n, chunk 4 ks + G (swizzled by the row)
-    auto addr = [&](int i) {
+    // read i = 2 ks + kb: key row 16 kb + n, chunk 4 ks + G
+    auto rd = [&](int i) {
       const int kb = i & 1, ks = i >> 1;
-      const int key = 16 * kb + n, c = 4 * ks + G;
-      return (const bf16x8*)(rowtile + key * (R * 2) + 16 * ((c & ~15) | ((c & 15) ^ (key & 15))));
+      const int c = 4 * ks + G;
+      return lds_read16(tile + (16 * kb + n) * (R * 2) + 16 * ((c & ~15) | ((c & 15) ^ f)));
     };
     constexpr int NR = 2 * NKS, DEPTH = 3;  // LDS reads kept in flight ahead of their use
     bf16x8 ring[DEPTH];
 #pragma unroll
-    for (int i = 0; i < DEPTH; ++i) ring[i] = *addr(i);
+    for (int i = 0; i < DEPTH; ++i) ring[i] = rd(i);
 #pragma unroll
     for (int i = 0; i < NR; ++i) {
       const bf16x8 av = ring[i % DEPTH];
-      if (i + DEPTH < NR) ring[i % DEPTH] = *addr(i + DEPTH);
+      if (i + DEPTH < NR) ring[i % DEPTH] = rd(i + DEPTH);
       const int kb = i & 1, ks = i >> 1;
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) s[kb][qb] = mfma16x16x32(av, qf[qb][ks], s[kb][qb]);
-      // keep each read DEPTH steps ahead of its use; vector ops may move freely
       __builtin_amdgcn_sched_barrier(0x0002 | 0x0400);
     }
   }
 
-  // Online-softmax update of both query rows of the lane for one tile.  The
-  // scores are already in log2 units (q_lat carries scale * log2 e).
-  // lim[qb]: keys with offset 16 kb + v (from k0 + 4 G) above lim are masked.
-  static __device__ __forceinline__ void softmax(const f32x4 (&s)[2][2], const int (&lim)[2],
-                                                 float (&m_run)[2], float (&l_run)[2], float (&alpha)[2],
-                                                 bool& grow_any, bf16x8 (&P)[2]) {
-    grow_any = false;
+  // Online-softmax update of the lane's two own rows for one tile (scores in
+  // log2 units: q_lat carries scale * log2 e).  Keys 16 kb + v (from
+  // k0 + 4 G) above lim[qb] are masked.
+  static __device__ __forceinline__ void softmax(const f32x4 (&s)[2][2], const int (&lim)[2], float (&m_run)[2],
+                                                 float (&l_run)[2], float (&alpha)[2], bf16x8 (&P)[2]) {
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
       float x[8];
@@ -251,97 +180,67 @@ struct Flash {
       float mt = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])), fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
       mt = max_xor32(max_xor16(mt));
       const bool grow = mt > m_run[qb] + kRescaleSlack;
-      alpha[qb] = grow ? exp2f(m_run[qb] - mt) : 1.f;
+      alpha[qb] = grow ? fast_exp2(m_run[qb] - mt) : 1.f;
       m_run[qb] = grow ? mt : m_run[qb];
-      grow_any |= grow;
       const float msub = m_run[qb] == -INFINITY ? 0.f : m_run[qb];
       float ps = 0.f;
+      uint32_t pk[4];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const float p = exp2f(x[u] - msub);
-        ps += p;
-        P[qb][u] = (__bf16)p;
+      for (int u = 0; u < 8; u += 2) {
+        const float p0 = fast_exp2(x[u] - msub), p1 = fast_exp2(x[u + 1] - msub);
+        ps += p0 + p1;
+        pk[u >> 1] = pack_bf16x2(p0, p1);
       }
       l_run[qb] = l_run[qb] * alpha[qb] + ps;
-    }
-  }
-
-  static __device__ __forceinline__ void rescale(f32x4 (&o)[NOB][2], const float (&alpha)[2]) {
-    mfma_agpr_wait();
-#pragma unroll
-    for (int c = 0; c < NOB; ++c)
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {  // a few registers at a time
-        mfma_agpr_tie(o[c][qb]);
-        o[c][qb] *= alpha[qb];
-        mfma_agpr_tie(o[c][qb]);
-      }
-  }
-
-  // O^T += L^T P^T from the transposed tile ([4][R][8] image).
-  static __device__ __forceinline__ void pv(const char* ttile, bf16x8 (&P)[2], f32x4 (&o)[NOB][2]) {
-    const int lane = threadIdx.x & 63;
-    const int G = lane >> 4, n = lane & 15;
-    const char* pa = ttile + G * (R * 16) + 16 * n;
-    constexpr int DEPTH = 4;  // LDS reads kept in flight ahead of their use
-    bf16x8 ring[DEPTH];
-#pragma unroll
-    for (int i = 0; i < DEPTH; ++i) ring[i] = *(const bf16x8*)(pa + 256 * i);
-    mfma_operand_ready(P[0]);
-    mfma_operand_ready(P[1]);
-#pragma unroll
-    for (int c = 0; c < NOB; ++c) {
-      const bf16x8 av = ring[c % DEPTH];
-      if (c + DEPTH < NOB) ring[c % DEPTH] = *(const bf16x8*)(pa + 256 * (c + DEPTH));
-      mfma16x16x32_a(o[c][0], av, P[0]);
-      mfma16x16x32_a(o[c][1], av, P[1]);
+      P[qb] = __builtin_bit_cast(bf16x8, u32x4{pk[0], pk[1], pk[2], pk[3]});
     }
   }
 };
 
 // q_lat, o_lat: [B][T*H][R] bf16 (row t*H + h of batch b; q_lat pre-scaled by
-// scale * log2 e); lat: [B][T][R];
-// latT: [B][ceil(T/32)][R][32] (latent_transpose).  One block = 128
-// consecutive (t, h) rows of one batch = 4 waves x 32 rows; all heads in the
-// block share each latent tile.  Per tile j the wave computes the softmax of
-// tile j while the scores of tile j+1 run on the matrix unit, then P_j L_j.
-// Row-major tiles (two buffers) and transposed tiles (three buffers) are
-// both copied two tiles ahead.  Blocks are issued heaviest (largest t) first.
+// scale * log2 e); lat: [B][T][R].  Per tile j the wave computes the softmax
+// of tile j while the scores of tile j+1 run on the matrix unit, posts P_j,
+// then accumulates P_j L_j for its columns.  Tiles are copied three ahead;
+// blocks are issued heaviest (largest t) first.
 template <int R>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
 void flash_latent_bf16(const uint16_t* __restrict__ q_lat, const uint16_t* __restrict__ lat,
-                       const uint16_t* __restrict__ latT, uint16_t* __restrict__ o_lat, int B,
-                       int T, int H) {
+                       uint16_t* __restrict__ o_lat, int B, int T, int H) {
   using F = Flash<R>;
-  constexpr int TILE_BYTES = 32 * R * 2;
+  constexpr int TILE = kTileKeys * R * 2;
+  constexpr int NI = TILE / 1024 / 4;  // copy instructions per wave and tile
+  static_assert(kFlashBufs == 4, "three tiles in flight");
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  char* rowbuf = smem;                      // [2][TILE_BYTES]
-  char* tbuf = smem + 2 * TILE_BYTES;       // [3][TILE_BYTES]
+  char* pbuf = smem + kFlashBufs * TILE;         // [8 q][64 lanes] x 16 bytes of P
+  float* abuf = (float*)(pbuf + F::NQ * 1024);   // [8 q][16] rescale factors, then l
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int G = lane >> 4, n = lane & 15;
   const long TH = (long)T * H;
   const int nrb = (int)((TH + 127) / 128);
-  const int nt = (T + 31) / 32;
   const int rb = nrb - 1 - (int)(blockIdx.x / B);
   const int b = blockIdx.x % B;
   const long row0 = (long)rb * 128;
   const long row_end = TH < row0 + 128 ? TH : row0 + 128;
   const int t_last_blk = (int)((row_end - 1) / H);
-  const int ntiles = t_last_blk / 32 + 1;
+  const int ntiles = t_last_blk / kTileKeys + 1;
+  // rows owned for the scores: 32 w .. 32 w + 31 of the block
   const long wrow0 = row0 + 32 * w;
-  const bool wactive = wrow0 < TH;
-  const int t_first_w = wactive ? (int)(wrow0 / H) : 0;
-  const int t_last_w = wactive ? (int)(((TH < wrow0 + 32 ? TH : wrow0 + 32) - 1) / H) : -1;
+  const int t_first_w = (int)((wrow0 < TH ? wrow0 : TH - 1) / H);
   long my_row[2];
   int t_row[2];
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
     my_row[qb] = wrow0 + 16 * qb + n;
-    const long crow = my_row[qb] < TH ? my_row[qb] : TH - 1;
-    t_row[qb] = (int)(crow / H);
+    t_row[qb] = (int)((my_row[qb] < TH ? my_row[qb] : TH - 1) / H);
   }
+  const uint16_t* latb = lat + (size_t)b * T * R;
+  const uint32_t lds0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)smem);
 
+  // first tiles in flight while the queries load
+#pragma unroll
+  for (int t = 0; t < kFlashBufs - 1; ++t)
+    if (t < ntiles) dma_tile32<R>(latb, kTileKeys * t, T, lds0 + t * TILE, w);
   bf16x8 qf[2][F::NKS];
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
@@ -350,81 +249,118 @@ void flash_latent_bf16(const uint16_t* __restrict__ q_lat, const uint16_t* __res
 #pragma unroll
     for (int ks = 0; ks < F::NKS; ++ks) qf[qb][ks] = *(const bf16x8*)(qrow + 32 * ks);
   }
-  f32x4 o[F::NOB][2];
+  // Consume the query registers before the loop: the copies are invisible to
+  // the compiler's wait counting, and a query load still pending at the loop
+  // head would make it wait on the vector-memory counter every iteration.
 #pragma unroll
-  for (int c = 0; c < F::NOB; ++c) o[c][0] = o[c][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
+  for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+    for (int ks = 0; ks < F::NKS; ++ks) asm volatile("" : : "v"(qf[qb][ks]));
 
-  const uint16_t* latb = lat + (size_t)b * T * R;
-  const uint16_t* latTb = latT + (size_t)b * nt * R * 32;
-  dma_rowtile<R>(latb, 0, T, rowbuf, w);
-  dma_tileT<R>(latTb, tbuf, w);
-  if (ntiles > 1) {
-    dma_rowtile<R>(latb, 32, T, rowbuf + TILE_BYTES, w);
-    dma_tileT<R>(latTb + (size_t)R * 32, tbuf + TILE_BYTES, w);
-  }
-  wait_all_memory();
-  __syncthreads();
+  f32x4 o[F::NCW][F::NQ];
+#pragma unroll
+  for (int c = 0; c < F::NCW; ++c)
+#pragma unroll
+    for (int q = 0; q < F::NQ; ++q) o[c][q] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
+  const int cw = w * (R / 4);
+  const TileCols<R> cols;
+
+  // tiles 0 and 1 landed (tile 2 may still be in flight)
+  if (ntiles > 2)
+    dma_wait<NI>();
+  else
+    dma_wait<0>();
+  __builtin_amdgcn_s_barrier();
   f32x4 s_cur[2][2];
-  F::scores(rowbuf, qf, s_cur);
-  __syncthreads();  // row tile 0 is refilled below
+  F::scores(smem, qf, s_cur);
   for (int j = 0; j < ntiles; ++j) {
-    // tiles j+2 (both orientations) are copied during this iteration; at
-    // its end only the copies issued one iteration earlier must have landed
-    const bool ahead = j + 2 < ntiles;
-    if (ahead) {
-      dma_tileT<R>(latTb + (size_t)(j + 2) * R * 32, tbuf + ((j + 2) % 3) * TILE_BYTES, w);
-      dma_rowtile<R>(latb, 32 * (j + 2), T, rowbuf + (j & 1) * TILE_BYTES, w);
-    }
-    const int k0 = 32 * j;
-    const bool act = k0 <= t_last_w;
-    const bool need_mask = k0 + 31 > t_first_w;
+    // the buffer of tile j - 1 is free: every wave passed the barrier that ended iteration j - 1
+    if (j + kFlashBufs - 1 < ntiles)
+      dma_tile32<R>(latb, kTileKeys * (j + kFlashBufs - 1), T, lds0 + ((j + kFlashBufs - 1) % kFlashBufs) * TILE, w);
+    const int k0 = kTileKeys * j;
+    const bool need_mask = k0 + kTileKeys - 1 > t_first_w;
     int lim[2];
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) lim[qb] = need_mask ? t_row[qb] - k0 - 4 * G : 1 << 30;
-    // Softmax of tile j (vector ALU) next to the scores of tile j+1 (matrix
-    // unit).  Both run unconditionally: a tile past the wave's rows is fully
-    // masked (p = 0, state unchanged); the scores after the last tile read a
-    // stale buffer and are discarded.
     bf16x8 P[2];
     float alpha[2];
-    bool grow_any;
-    F::softmax(s_cur, lim, m_run, l_run, alpha, grow_any, P);
+    F::softmax(s_cur, lim, m_run, l_run, alpha, P);
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      *(__attribute__((address_space(3))) bf16x8*)(uintptr_t)(pbuf + ((2 * w + qb) * 64 + lane) * 16) = P[qb];
+      if (G == 0) abuf[(2 * w + qb) * 16 + n] = alpha[qb];
+    }
+    // scores of tile j + 1 (after the last tile: a stale buffer, discarded)
     f32x4 s_next[2][2];
-    F::scores(rowbuf + ((j + 1) & 1) * TILE_BYTES, qf, s_next);
-    if (act) {
-      if (__builtin_amdgcn_ballot_w64(grow_any)) F::rescale(o, alpha);
-      F::pv(tbuf + (j % 3) * TILE_BYTES, P, o);
+    F::scores(smem + ((j + 1) % kFlashBufs) * TILE, qf, s_next);
+    __builtin_amdgcn_s_barrier();  // P and rescale factors of tile j posted
+    {
+      float al[F::NQ];
+      bool grow = false;
+#pragma unroll
+      for (int q = 0; q < F::NQ; ++q) {
+        al[q] = abuf[q * 16 + n];
+        grow |= al[q] != 1.f;
+      }
+      if (__builtin_amdgcn_ballot_w64(grow)) {
+        mfma_agpr_wait();
+#pragma unroll
+        for (int c = 0; c < F::NCW; ++c)
+#pragma unroll
+          for (int q = 0; q < F::NQ; ++q) {  // a few registers at a time
+            mfma_agpr_tie(o[c][q]);
+            o[c][q] *= al[q];
+            mfma_agpr_tie(o[c][q]);
+          }
+      }
+    }
+    {
+      bf16x8 pq[F::NQ];
+#pragma unroll
+      for (int q = 0; q < F::NQ; ++q) pq[q] = lds_read16(pbuf + (q * 64 + lane) * 16);
+      const char* tile = smem + (j % kFlashBufs) * TILE;
+      bf16x8 a_next = cols(tile, cw);
+#pragma unroll
+      for (int c = 0; c < F::NCW; ++c) {
+        const bf16x8 av = a_next;
+        if (c + 1 < F::NCW) a_next = cols(tile, cw + 16 * (c + 1));
+#pragma unroll
+        for (int q = 0; q < F::NQ; ++q) mfma16x16x32_a(o[c][q], av, pq[q]);
+      }
     }
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) s_cur[kb][qb] = s_next[kb][qb];
-    if (ahead)
-      wait_vmem_outstanding<2 * (32 * R * 2 / 1024 / 4)>();  // tiles j+2 may stay in flight
+    // own part of tile j + 2 landed before the barrier that ends the iteration
+    if (j + kFlashBufs - 1 < ntiles)
+      dma_wait<NI>();
     else
-      wait_all_memory();
-    // a bare barrier: __syncthreads() would also wait for the copy still in flight
+      dma_wait<0>();
     __builtin_amdgcn_s_barrier();
   }
-  if (!wactive) return;
+
+  // ---- l of every row through LDS, then the normalised rows of this wave's columns
   mfma_agpr_wait();
-#pragma unroll
-  for (int c = 0; c < F::NOB; ++c) {
-    mfma_agpr_tie(o[c][0]);
-    mfma_agpr_tie(o[c][1]);
-  }
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
     float lt = l_run[qb] + __shfl_xor(l_run[qb], 16);
     lt += __shfl_xor(lt, 32);
-    const float inv = 1.f / lt;
-    if (my_row[qb] >= TH) continue;
-    uint16_t* orow = o_lat + ((size_t)b * TH + my_row[qb]) * R + 4 * G;
+    if (G == 0) abuf[(2 * w + qb) * 16 + n] = lt;
+  }
+  __syncthreads();
 #pragma unroll
-    for (int c = 0; c < F::NOB; ++c) {
-      u32x2 v = {pack_bf16x2(o[c][qb][0] * inv, o[c][qb][1] * inv),
-                 pack_bf16x2(o[c][qb][2] * inv, o[c][qb][3] * inv)};
+  for (int q = 0; q < F::NQ; ++q) {
+    const long row = row0 + 16 * q + n;
+    const float inv = 1.f / abuf[q * 16 + n];
+    if (row >= TH) continue;
+    uint16_t* orow = o_lat + ((size_t)b * TH + row) * R + cw + 4 * G;
+#pragma unroll
+    for (int c = 0; c < F::NCW; ++c) {
+      mfma_agpr_tie(o[c][q]);
+      const u32x2 v = {pack_bf16x2(o[c][q][0] * inv, o[c][q][1] * inv),
+                       pack_bf16x2(o[c][q][2] * inv, o[c][q][3] * inv)};
       *(u32x2*)(orow + 16 * c) = v;
     }
   }
@@ -435,10 +371,8 @@ void flash_latent_bf16(const uint16_t* __restrict__ q_lat, const uint16_t* __res
 template <int R>
 static hipError_t run_prefill(const uint16_t* q, const uint16_t* lat, const uint16_t* wk,
                               const uint16_t* wv, uint16_t* out, int B, int T, int H, int d,
-                              float sl2, uint16_t* q_lat, uint16_t* o_lat, uint16_t* wvT,
-                              uint16_t* latT, hipStream_t st) {
+                              float sl2, uint16_t* q_lat, uint16_t* o_lat, uint16_t* wvT, hipStream_t st) {
   const int N = B * T;
-  const int nt = (T + 31) / 32;
   static bool attr_set = false;
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute((const void*)flash_latent_bf16<R>,
@@ -453,16 +387,12 @@ static hipError_t run_prefill(const uint16_t* q, const uint16_t* lat, const uint
     e = transpose_wv_launch(wv, wvT, R, H, d, st);
     if (e != hipSuccess) return e;
   }
-  {
-    ProfScope ps("latent_transpose", st);
-    hipLaunchKernelGGL(latent_transpose<R>, dim3(nt, B), dim3(256), 0, st, lat, latT, T, nt);
-  }
   const long TH = (long)T * H;
   const int nrb = (int)((TH + 127) / 128);
   {
     ProfScope ps("flash_latent_bf16", st);
-    hipLaunchKernelGGL(flash_latent_bf16<R>, dim3(B * nrb), dim3(256), flash_lds_bytes(R), st, q_lat,
-                       lat, latT, o_lat, B, T, H);
+    hipLaunchKernelGGL(flash_latent_bf16<R>, dim3(B * nrb), dim3(256), flash_lds_bytes(R), st, q_lat, lat, o_lat,
+                       B, T, H);
   }
   {
     ProfScope ps("up_bf16", st);
@@ -471,15 +401,15 @@ static hipError_t run_prefill(const uint16_t* q, const uint16_t* lat, const uint
   return hipGetLastError();
 }
 
+// Workspace: q_lat [B*T*H][r] | o_lat [B*T*H][r] | W_uv^T [H][d][r], all bf16.
 hipError_t prefill_mfma(const void* q, const void* lat, const void* wk, const void* wv, void* out,
                         int B, int T, int H, int d, int r, float sl2, void* ws, hipStream_t st) {
   const size_t rows = (size_t)B * T * H;
   uint16_t* q_lat = (uint16_t*)ws;
   uint16_t* o_lat = q_lat + rows * r;
   uint16_t* wvT = o_lat + rows * r;
-  uint16_t* latT = wvT + (size_t)H * d * r;
 #define ARGS (const uint16_t*)q, (const uint16_t*)lat, (const uint16_t*)wk, (const uint16_t*)wv, \
-             (uint16_t*)out, B, T, H, d, sl2, q_lat, o_lat, wvT, latT, st
+             (uint16_t*)out, B, T, H, d, sl2, q_lat, o_lat, wvT, st
   switch (r) {
     case 128: return run_prefill<128>(ARGS);
     case 256: return run_prefill<256>(ARGS);
@@ -491,8 +421,7 @@ hipError_t prefill_mfma(const void* q, const void* lat, const void* wk, const vo
 
 size_t prefill_mfma_workspace(int B, int T, int H, int d, int r) {
   const size_t rows = (size_t)B * T * H;
-  const size_t nt = ((size_t)T + 31) / 32;
-  return (2 * rows * r + (size_t)H * d * r + (size_t)B * nt * 32 * r) * 2;
+  return (2 * rows * r + (size_t)H * d * r) * 2;
 }
 
 }  // namespace mla

@@ -1,0 +1,85 @@
+// Latent tiles in LDS, shared by the prefill and decode kernels: LDS-DMA
+// copies issued as inline assembly, and the swizzled row-major 32-key tile
+// that serves both the score reads (16-byte rows) and the transpose reads
+// of the P * latent product.
+#pragma once
+
+#include "mla_device.h"
+
+namespace mla {
+
+constexpr int kTileKeys = 32;  // keys per latent tile
+
+// LDS-DMA copy of 16 bytes per lane (lane l: gptr -> LDS byte lds_base + 16 l).
+// Issued as inline assembly: the compiler then cannot pair every later LDS
+// transpose read with a wait for all copies in flight (it cannot tell which
+// LDS bytes a copy writes), which would serialise the prefetch.  The kernel
+// orders copies and reads itself with dma_wait<n>().
+__device__ __forceinline__ void dma16(const void* gptr, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(gptr), "s"(lds_base)
+               : "memory", "m0");
+}
+// Wait until at most n of this wave's vector-memory operations are outstanding.
+template <int n>
+__device__ __forceinline__ void dma_wait() {
+  static_assert(n >= 0 && n < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" : : "n"(n) : "memory");
+}
+
+// Block-shared tile of 32 keys, row-major, 16-byte chunks XOR-swizzled by
+// tswz(key) inside every 16-chunk group:
+//   - score reads (16 lanes = 16 consecutive keys, one chunk each) hit 16
+//     distinct slots because tswz is a permutation of 0..15 on key % 16;
+//   - transpose reads (32 lanes = 8 consecutive keys x one chunk pair) hit 16
+//     distinct slots because tswz(key) >> 1 is a permutation of key % 8.
+__device__ __forceinline__ int tswz(int key) { return ((key & 7) << 1) | ((key >> 3) & 1); }
+
+// Wave w's share of the LDS-DMA copy of one tile: instructions i = w, w + 4, ...
+// of the tile's 32 R * 2 / 1024, each 64 lanes x 16 bytes.  The swizzle is
+// applied on the global side: LDS-DMA writes lane l to byte 16 l of its
+// 1 KB destination, so lane l fetches the chunk that belongs there.
+template <int R>
+__device__ __forceinline__ void dma_tile32(const uint16_t* latb, int k0, int kend, uint32_t tile, int w) {
+  constexpr int NC = R / 8;                                   // chunks per key row
+  constexpr int NI = kTileKeys * R * 2 / 1024 / 4;      // instructions per wave
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int ins = 4 * i + w;
+    const int idx = ins * 64 + lane;
+    const int s = idx / NC, p = idx % NC;
+    const int c = (p & ~15) | ((p & 15) ^ tswz(s));
+    const int key = k0 + s < kend ? k0 + s : kend - 1;
+    dma16(latb + (size_t)key * R + 8 * c, tile + ins * 1024);
+  }
+}
+
+// A operand of O^T += L^T P^T (16x16x32) for tile columns [c0, c0 + 16),
+// c0 a multiple of 16: lane (G, n) receives L^T[c0 + n][key] for the keys
+// 4 G + u and 16 + 4 G + u, u = 0..3 (the k-slot order of the P operand),
+// from two transpose reads.  Transpose read t of lane (G, n) addresses key
+// 16 t + 4 G + n / 4, columns c0 + 4 (n % 4) .. + 3.
+template <int R>
+struct TileCols {
+  int key_off, fk, sub, half;
+  __device__ __forceinline__ TileCols() {
+    const int lane = threadIdx.x & 63, G = lane >> 4, n = lane & 15;
+    const int key = 4 * G + (n >> 2);
+    key_off = key * (R * 2);
+    fk = tswz(key);  // equal for key + 16
+    sub = 8 * (n & 1);
+    half = (n & 3) >> 1;
+  }
+  __device__ __forceinline__ bf16x8 operator()(const char* tile, int c0) const {
+    const int ch = (c0 >> 3) + half;
+    const int off = key_off + 16 * ((ch & ~15) | ((ch & 15) ^ fk)) + sub;
+    const i16x4 a0 = lds_read_tr16(tile + off);
+    const i16x4 a1 = lds_read_tr16(tile + off + 16 * (R * 2));
+    return __builtin_bit_cast(bf16x8, u32x4{__builtin_bit_cast(u32x2, a0)[0], __builtin_bit_cast(u32x2, a0)[1],
+                                            __builtin_bit_cast(u32x2, a1)[0], __builtin_bit_cast(u32x2, a1)[1]});
+  }
+};
+
+}  // namespace mla

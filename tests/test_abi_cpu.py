@@ -87,11 +87,10 @@ def test_down_proj_errors():
 def test_workspace_sizes():
     # float32 path: q_lat and o_lat in float32
     assert mla.mla_latent_attn_workspace_size(2, 64, 4, 32, 32, F32) == 2 * 2 * 64 * 4 * 32 * 4
-    # bf16 matrix-core path: q_lat, o_lat in bf16, W_uv^T, and the transposed latent tiles
+    # bf16 matrix-core path: q_lat, o_lat in bf16 and W_uv^T
     rows = 8 * 2048 * 16
-    latT = 8 * (2048 // 32) * 32 * 512
     assert mla.mla_latent_attn_workspace_size(8, 2048, 16, 128, 512, BF16) == \
-        (2 * rows * 512 + 16 * 128 * 512 + latT) * 2
+        (2 * rows * 512 + 16 * 128 * 512) * 2
     assert mla.mla_latent_attn_workspace_size(0, 1, 1, 1, 1, F32) == 0
     assert mla.mla_decode_workspace_size(64, 8192, 32, 128, 512, BF16) > 64 * 32 * 512 * 4
     assert mla.mla_decode_workspace_size(1, 1, 1, 1, 1, 9) == 0
