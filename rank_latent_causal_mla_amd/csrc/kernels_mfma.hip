@@ -166,22 +166,26 @@ struct Flash {
   }
 
   // Online-softmax update of the lane's two own rows for one tile (scores in
-  // log2 units: q_lat carries scale * log2 e).  Keys 16 kb + v (from
-  // k0 + 4 G) above lim[qb] are masked.
-  static __device__ __forceinline__ void softmax(const f32x4 (&s)[2][2], const int (&lim)[2], float (&m_run)[2],
+  // log2 units: q_lat carries scale * log2 e).  With MASK, keys 16 kb + v
+  // (from k0 + 4 G) above lim[qb] are masked.  Returns whether any row's
+  // running max moved (then alpha != 1 for it).
+  template <bool MASK>
+  static __device__ __forceinline__ bool softmax(const f32x4 (&s)[2][2], const int (&lim)[2], float (&m_run)[2],
                                                  float (&l_run)[2], float (&alpha)[2], bf16x8 (&P)[2]) {
+    bool grow_any = false;
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
       float x[8];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int v = 0; v < 4; ++v) x[4 * kb + v] = (16 * kb + v > lim[qb]) ? -INFINITY : s[kb][qb][v];
+        for (int v = 0; v < 4; ++v) x[4 * kb + v] = (MASK && 16 * kb + v > lim[qb]) ? -INFINITY : s[kb][qb][v];
       float mt = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])), fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
       mt = max_xor32(max_xor16(mt));
       const bool grow = mt > m_run[qb] + kRescaleSlack;
       alpha[qb] = grow ? fast_exp2(m_run[qb] - mt) : 1.f;
       m_run[qb] = grow ? mt : m_run[qb];
+      grow_any |= grow;
       const float msub = m_run[qb] == -INFINITY ? 0.f : m_run[qb];
       float ps = 0.f;
       uint32_t pk[4];
@@ -194,6 +198,7 @@ struct Flash {
       l_run[qb] = l_run[qb] * alpha[qb] + ps;
       P[qb] = __builtin_bit_cast(bf16x8, u32x4{pk[0], pk[1], pk[2], pk[3]});
     }
+    return grow_any;
   }
 };
 
@@ -213,6 +218,7 @@ void flash_latent_bf16(const uint16_t* __restrict__ q_lat, const uint16_t* __res
   extern __shared__ __attribute__((aligned(16))) char smem[];
   char* pbuf = smem + kFlashBufs * TILE;         // [8 q][64 lanes] x 16 bytes of P
   float* abuf = (float*)(pbuf + F::NQ * 1024);   // [8 q][16] rescale factors, then l
+  int* fbuf = (int*)(abuf + F::NQ * 16);         // [4]: wave w's rows rescale this tile
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int G = lane >> 4, n = lane & 15;
@@ -275,35 +281,31 @@ void flash_latent_bf16(const uint16_t* __restrict__ q_lat, const uint16_t* __res
   f32x4 s_cur[2][2];
   F::scores(smem, qf, s_cur);
   for (int j = 0; j < ntiles; ++j) {
-    // the buffer of tile j - 1 is free: every wave passed the barrier that ended iteration j - 1
-    if (j + kFlashBufs - 1 < ntiles)
-      dma_tile32<R>(latb, kTileKeys * (j + kFlashBufs - 1), T, lds0 + ((j + kFlashBufs - 1) % kFlashBufs) * TILE, w);
     const int k0 = kTileKeys * j;
-    const bool need_mask = k0 + kTileKeys - 1 > t_first_w;
     int lim[2];
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) lim[qb] = need_mask ? t_row[qb] - k0 - 4 * G : 1 << 30;
+    for (int qb = 0; qb < 2; ++qb) lim[qb] = t_row[qb] - k0 - 4 * G;
     bf16x8 P[2];
     float alpha[2];
-    F::softmax(s_cur, lim, m_run, l_run, alpha, P);
+    const bool grow = k0 + kTileKeys - 1 > t_first_w ? F::template softmax<true>(s_cur, lim, m_run, l_run, alpha, P)
+                                                     : F::template softmax<false>(s_cur, lim, m_run, l_run, alpha, P);
+    // every wave passed the barrier that ended iteration j - 1: the exchange buffers are free
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
       *(__attribute__((address_space(3))) bf16x8*)(uintptr_t)(pbuf + ((2 * w + qb) * 64 + lane) * 16) = P[qb];
       if (G == 0) abuf[(2 * w + qb) * 16 + n] = alpha[qb];
     }
+    if (lane == 0) fbuf[w] = __builtin_amdgcn_ballot_w64(grow) != 0;
     // scores of tile j + 1 (after the last tile: a stale buffer, discarded)
     f32x4 s_next[2][2];
     F::scores(smem + ((j + 1) % kFlashBufs) * TILE, qf, s_next);
     __builtin_amdgcn_s_barrier();  // P and rescale factors of tile j posted
     {
-      float al[F::NQ];
-      bool grow = false;
+      const u32x4 f = *(const __attribute__((address_space(3))) u32x4*)(uintptr_t)fbuf;
+      if ((f[0] | f[1] | f[2] | f[3]) != 0) {  // some row of the block has a new max
+        float al[F::NQ];
 #pragma unroll
-      for (int q = 0; q < F::NQ; ++q) {
-        al[q] = abuf[q * 16 + n];
-        grow |= al[q] != 1.f;
-      }
-      if (__builtin_amdgcn_ballot_w64(grow)) {
+        for (int q = 0; q < F::NQ; ++q) al[q] = abuf[q * 16 + n];
         mfma_agpr_wait();
 #pragma unroll
         for (int c = 0; c < F::NCW; ++c)
@@ -329,6 +331,9 @@ void flash_latent_bf16(const uint16_t* __restrict__ q_lat, const uint16_t* __res
         for (int q = 0; q < F::NQ; ++q) mfma16x16x32_a(o[c][q], av, pq[q]);
       }
     }
+    // refill the buffer of tile j - 1 (every wave is past it) while the matrix ops run
+    if (j + kFlashBufs - 1 < ntiles)
+      dma_tile32<R>(latb, kTileKeys * (j + kFlashBufs - 1), T, lds0 + ((j + kFlashBufs - 1) % kFlashBufs) * TILE, w);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll

@@ -10,16 +10,24 @@ namespace mla {
 
 constexpr int kTileKeys = 32;  // keys per latent tile
 
-// LDS-DMA copy of 16 bytes per lane (lane l: gptr -> LDS byte lds_base + 16 l).
-// Issued as inline assembly: the compiler then cannot pair every later LDS
-// transpose read with a wait for all copies in flight (it cannot tell which
-// LDS bytes a copy writes), which would serialise the prefetch.  The kernel
-// orders copies and reads itself with dma_wait<n>().
-__device__ __forceinline__ void dma16(const void* gptr, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-               :
-               : "v"(gptr), "s"(lds_base)
-               : "memory", "m0");
+// LDS-DMA copy of 16 bytes per lane: lane l copies global byte
+// gbase + voff(l) to LDS byte lds_base + 16 l (gbase and lds_base
+// wave-uniform).  Issued as inline assembly: the compiler then cannot pair
+// every later LDS transpose read with a wait for all copies in flight (it
+// cannot tell which LDS bytes a copy writes), which would serialise the
+// prefetch.  The kernel orders copies and reads itself with dma_wait<n>().
+// M0 carries the LDS address; its previous value is restored.
+__device__ __forceinline__ void dma16(const void* gbase, uint32_t voff, uint32_t lds_base) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, %2\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(voff), "s"(gbase), "s"(lds_base)
+      : "memory");
 }
 // Wait until at most n of this wave's vector-memory operations are outstanding.
 template <int n>
@@ -42,17 +50,21 @@ __device__ __forceinline__ int tswz(int key) { return ((key & 7) << 1) | ((key >
 // 1 KB destination, so lane l fetches the chunk that belongs there.
 template <int R>
 __device__ __forceinline__ void dma_tile32(const uint16_t* latb, int k0, int kend, uint32_t tile, int w) {
-  constexpr int NC = R / 8;                                   // chunks per key row
-  constexpr int NI = kTileKeys * R * 2 / 1024 / 4;      // instructions per wave
+  constexpr int NC = R / 8;    // 16-byte chunks per key row
+  constexpr int RPI = 64 / NC;  // key rows per instruction
+  constexpr int NI = kTileKeys * R * 2 / 1024 / 4;  // instructions per wave
+  static_assert(NC <= 64 && 64 % NC == 0, "a copy instruction covers whole rows");
   const int lane = threadIdx.x & 63;
+  const int sl = lane / NC, p = lane % NC;
 #pragma unroll
   for (int i = 0; i < NI; ++i) {
-    const int ins = 4 * i + w;
-    const int idx = ins * 64 + lane;
-    const int s = idx / NC, p = idx % NC;
+    const int ins = 4 * i + w;       // wave-uniform
+    const int r0 = ins * RPI;        // first row of the instruction
+    const int kb = __builtin_amdgcn_readfirstlane(k0 + r0 < kend ? k0 + r0 : kend - 1);
+    const int s = r0 + sl;           // row within the tile
     const int c = (p & ~15) | ((p & 15) ^ tswz(s));
     const int key = k0 + s < kend ? k0 + s : kend - 1;
-    dma16(latb + (size_t)key * R + 8 * c, tile + ins * 1024);
+    dma16(latb + (size_t)kb * R, (uint32_t)((key - kb) * R * 2 + 16 * c), tile + ins * 1024);
   }
 }
 

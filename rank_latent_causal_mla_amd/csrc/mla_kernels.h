@@ -17,8 +17,8 @@ size_t decode_max_splits(int B);
 constexpr size_t decode_lds_bytes(int R) { return (size_t)4 * 32 * R * 2 + 2048 + 256; }
 
 // LDS of the prefill flash kernel: a ring of four 32-key latent tiles, one
-// tile's probabilities for 128 rows (8 KB) and 128 rescale factors.
-constexpr size_t flash_lds_bytes(int R) { return (size_t)4 * 32 * R * 2 + 8 * 1024 + 8 * 16 * 4; }
+// tile's probabilities for 128 rows (8 KB), 128 rescale factors and 4 flags.
+constexpr size_t flash_lds_bytes(int R) { return (size_t)4 * 32 * R * 2 + 8 * 1024 + 8 * 16 * 4 + 16; }
 
 // ---- bf16 matrix-core path (r in {128, 256, 512}, d in {32, 64, 128, 256})
 bool mfma_supported(int d, int r);
