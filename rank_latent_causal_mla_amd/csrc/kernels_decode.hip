@@ -277,7 +277,7 @@ __global__ __launch_bounds__(256) void decode_prep(const uint16_t* __restrict__ 
     length_prefix_block(lens, B, Tmax, S);
   } else if (bid <= nabs) {
     const int t = bid - 1;
-    absorb_tile<R, DK, 1>(q, wk, q_lat, B, H, qscale, t / (H * NQ), (t / NQ) % H, 128 * (t % NQ));
+    absorb_tile<R, DK, 1>(q, wk, q_lat, B, H, qscale, t / (H * NQ), 1, (t / NQ) % H, 128 * (t % NQ));
   } else {
     const int t = bid - 1 - nabs;
     const int nrb = R / 32, neb = (d + 31) / 32;

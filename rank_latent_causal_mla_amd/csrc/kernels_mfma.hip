@@ -22,12 +22,19 @@ namespace mla {
 // ---------------------------------------------------------------------------
 // Absorption (one block per 32 query rows of one head, the whole rank) and
 // the W_uv transpose, as kernels around the block bodies of prep_blocks.h.
+// Row blocks of 32 rows per absorption block, and the rank slice per block.
+constexpr int kAbsorbRowBlocks = 8;
 template <int R, int DK>
-__global__ __launch_bounds__(256) void absorb_bf16(const uint16_t* __restrict__ q,
-                                                   const uint16_t* __restrict__ wk,
-                                                   uint16_t* __restrict__ q_lat, int N, int H,
-                                                   float qscale) {
-  absorb_tile<R, DK, R / 128>(q, wk, q_lat, N, H, qscale, blockIdx.x, blockIdx.y, 0);
+constexpr int absorb_nb() { return R / 128 < 32 / DK ? R / 128 : 32 / DK; }
+
+template <int R, int DK>
+__global__ __launch_bounds__(256, 2) void absorb_bf16(const uint16_t* __restrict__ q,
+                                                      const uint16_t* __restrict__ wk,
+                                                      uint16_t* __restrict__ q_lat, int N, int H,
+                                                      float qscale) {
+  constexpr int NB = absorb_nb<R, DK>();
+  absorb_tile<R, DK, NB>(q, wk, q_lat, N, H, qscale, blockIdx.x * kAbsorbRowBlocks, kAbsorbRowBlocks, blockIdx.y,
+                         128 * NB * blockIdx.z);
 }
 
 __global__ __launch_bounds__(256) void transpose_wv(const uint16_t* __restrict__ wv, uint16_t* __restrict__ wvT,
@@ -38,12 +45,12 @@ __global__ __launch_bounds__(256) void transpose_wv(const uint16_t* __restrict__
 template <int R>
 static hipError_t absorb_launch(const uint16_t* q, const uint16_t* wk, uint16_t* q_lat, int N, int H,
                                 int d, float qscale, hipStream_t st) {
-  const dim3 grid((N + 31) / 32, H);
+  const int nrb = (N + 32 * kAbsorbRowBlocks - 1) / (32 * kAbsorbRowBlocks);
   switch (d) {
-    case 32: hipLaunchKernelGGL((absorb_bf16<R, 2>), grid, dim3(256), 0, st, q, wk, q_lat, N, H, qscale); break;
-    case 64: hipLaunchKernelGGL((absorb_bf16<R, 4>), grid, dim3(256), 0, st, q, wk, q_lat, N, H, qscale); break;
-    case 128: hipLaunchKernelGGL((absorb_bf16<R, 8>), grid, dim3(256), 0, st, q, wk, q_lat, N, H, qscale); break;
-    case 256: hipLaunchKernelGGL((absorb_bf16<R, 16>), grid, dim3(256), 0, st, q, wk, q_lat, N, H, qscale); break;
+    case 32: hipLaunchKernelGGL((absorb_bf16<R, 2>), dim3(nrb, H, R / (128 * absorb_nb<R, 2>())), dim3(256), 0, st, q, wk, q_lat, N, H, qscale); break;
+    case 64: hipLaunchKernelGGL((absorb_bf16<R, 4>), dim3(nrb, H, R / (128 * absorb_nb<R, 4>())), dim3(256), 0, st, q, wk, q_lat, N, H, qscale); break;
+    case 128: hipLaunchKernelGGL((absorb_bf16<R, 8>), dim3(nrb, H, R / (128 * absorb_nb<R, 8>())), dim3(256), 0, st, q, wk, q_lat, N, H, qscale); break;
+    case 256: hipLaunchKernelGGL((absorb_bf16<R, 16>), dim3(nrb, H, R / (128 * absorb_nb<R, 16>())), dim3(256), 0, st, q, wk, q_lat, N, H, qscale); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -67,44 +74,53 @@ hipError_t transpose_wv_launch(const uint16_t* wv, uint16_t* wvT, int R, int H, 
 
 // ---------------------------------------------------------------------------
 // Up-projection: out[n, h, e] = sum_rho o_lat[n*H + h, rho] * W_uv[rho, h, e],
-// computed as out^T = W_uv^T o_lat^T.  Block: 4 waves x 32 tokens of one head.
+// computed as out^T = W_uv^T o_lat^T.  Block: head h, row blocks
+// kUpRowBlocks * blockIdx.x .. of 32 rows; wave w takes the output blocks
+// e = 32 i .. 32 i + 31 for i = w, w + 4, ..., holding that slice of W_uv^T
+// in registers across the row blocks, so W_uv is read once per block.
+constexpr int kUpRowBlocks = 8;
 template <int R>
-__global__ __launch_bounds__(256) void up_bf16(const uint16_t* __restrict__ o_lat,
-                                               const uint16_t* __restrict__ wvT,
-                                               uint16_t* __restrict__ out, int N, int H, int d) {
+__global__ __launch_bounds__(256, 2) void up_bf16(const uint16_t* __restrict__ o_lat,
+                                                  const uint16_t* __restrict__ wvT,
+                                                  uint16_t* __restrict__ out, int N, int H, int d) {
+  constexpr int NKS = R / 16;  // contraction steps
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int g = lane >> 5, l32 = lane & 31;
   const int h = blockIdx.y;
-  const int n = blockIdx.x * 128 + w * 32 + l32;
-  if (blockIdx.x * 128 + w * 32 >= N) return;
-  const int nc = min(n, N - 1);
   const int neb = d / 32;
-  f32x16 acc[8];
+  const int nb0 = blockIdx.x * kUpRowBlocks;
+  for (int i = w; i < neb; i += 4) {
+    bf16x8 a[NKS];
+    const uint16_t* wrow = wvT + ((size_t)h * d + 32 * i + l32) * R + 8 * g;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) acc[i] = f32x16{};
-  const uint16_t* orow = o_lat + ((size_t)nc * H + h) * R + 8 * g;
-  const uint16_t* wrow = wvT + ((size_t)h * d + l32) * R + 8 * g;
-  for (int ks = 0; ks < R / 16; ++ks) {
-    const bf16x8 bo = *(const bf16x8*)(orow + 16 * ks);
+    for (int ks = 0; ks < NKS; ++ks) a[ks] = *(const bf16x8*)(wrow + 16 * ks);
+    for (int nb = nb0; nb < nb0 + kUpRowBlocks && nb * 32 < N; ++nb) {
+      const int n = nb * 32 + l32;
+      const uint16_t* orow = o_lat + ((size_t)min(n, N - 1) * H + h) * R + 8 * g;
+      f32x16 acc0 = f32x16{}, acc1 = f32x16{};
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-      if (i < neb) {
-        const bf16x8 a = *(const bf16x8*)(wrow + (size_t)32 * i * R + 16 * ks);
-        acc[i] = mfma32x32x16(a, bo, acc[i]);
+      for (int k8 = 0; k8 < NKS; k8 += 8) {  // eight operand loads ahead of their matrix ops
+        bf16x8 bo[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) bo[u] = *(const bf16x8*)(orow + 16 * (k8 + u));
+#pragma unroll
+        for (int u = 0; u < 8; u += 2) {
+          acc0 = mfma32x32x16(a[k8 + u], bo[u], acc0);
+          acc1 = mfma32x32x16(a[k8 + u + 1], bo[u + 1], acc1);
+        }
       }
+      if (n < N) {
+        uint16_t* dst = out + ((size_t)n * H + h) * d;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int e = 32 * i + 8 * j + 4 * g;
+          u32x2 v = {pack_bf16x2(acc0[4 * j] + acc1[4 * j], acc0[4 * j + 1] + acc1[4 * j + 1]),
+                     pack_bf16x2(acc0[4 * j + 2] + acc1[4 * j + 2], acc0[4 * j + 3] + acc1[4 * j + 3])};
+          *(u32x2*)(dst + e) = v;
+        }
+      }
+    }
   }
-  if (n >= N) return;
-  uint16_t* dst = out + ((size_t)n * H + h) * d;
-#pragma unroll
-  for (int i = 0; i < 8; ++i)
-    if (i < neb)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int e = 32 * i + 8 * j + 4 * g;
-        u32x2 v = {pack_bf16x2(acc[i][4 * j], acc[i][4 * j + 1]),
-                   pack_bf16x2(acc[i][4 * j + 2], acc[i][4 * j + 3])};
-        *(u32x2*)(dst + e) = v;
-      }
 }
 
 // ---------------------------------------------------------------------------
@@ -401,7 +417,8 @@ static hipError_t run_prefill(const uint16_t* q, const uint16_t* lat, const uint
   }
   {
     ProfScope ps("up_bf16", st);
-    hipLaunchKernelGGL(up_bf16<R>, dim3((N + 127) / 128, H), dim3(256), 0, st, o_lat, wvT, out, N, H, d);
+    hipLaunchKernelGGL(up_bf16<R>, dim3((N + 32 * kUpRowBlocks - 1) / (32 * kUpRowBlocks), H), dim3(256), 0, st, o_lat,
+                       wvT, out, N, H, d);
   }
   return hipGetLastError();
 }

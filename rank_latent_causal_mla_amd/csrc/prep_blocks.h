@@ -10,46 +10,54 @@ namespace mla {
 // Absorption: q_lat[n*H + h, rho] = qscale * sum_e W_uk[rho, h, e] * q[n, h, e]
 // (n = b*T + t; qscale folds the softmax scale and log2 e into q_lat).
 // Computed transposed, q_lat^T = W_h q_h^T, so each lane ends with 4
-// consecutive rho of one query row.  The block covers 32 query rows
-// (row block nb) of head h and the rank slice [rho_base, rho_base + 128 NB);
-// wave w takes 32 NB of those rho.  DK = d / 16 steps of the contraction,
-// all operands of a step loaded before its matrix ops.
+// consecutive rho of one query row.  The block covers head h, the rank slice
+// [rho_base, rho_base + 128 NB) (wave w takes 32 NB of those rho, its slice
+// of W_uk held in registers) and the row blocks nb0 .. nb0 + nbn - 1 of 32
+// query rows each, so W_uk is read once per block.  DK = d / 16 steps of
+// the contraction.
 template <int R, int DK, int NB>
 __device__ __forceinline__ void absorb_tile(const uint16_t* __restrict__ q, const uint16_t* __restrict__ wk,
-                                            uint16_t* __restrict__ q_lat, int N, int H, float qscale, int nb,
-                                            int h, int rho_base) {
+                                            uint16_t* __restrict__ q_lat, int N, int H, float qscale, int nb0,
+                                            int nbn, int h, int rho_base) {
   constexpr int d = 16 * DK;
+  static_assert(NB * DK <= 32, "the W_uk slice fits 128 registers");
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int g = lane >> 5, l32 = lane & 31;
-  const int n = nb * 32 + l32;
-  const int nc = min(n, N - 1);
   const int rho0 = rho_base + w * 32 * NB;
-  const uint16_t* qrow = q + ((size_t)nc * H + h) * d + 8 * g;
-  bf16x8 bq[DK];
-#pragma unroll
-  for (int ks = 0; ks < DK; ++ks) bq[ks] = *(const bf16x8*)(qrow + 16 * ks);
-  f32x16 acc[NB];
+  bf16x8 a[NB][DK];
 #pragma unroll
   for (int i = 0; i < NB; ++i) {
     const uint16_t* wrow = wk + ((size_t)(rho0 + 32 * i + l32) * H + h) * d + 8 * g;
-    bf16x8 a[DK];
 #pragma unroll
-    for (int ks = 0; ks < DK; ++ks) a[ks] = *(const bf16x8*)(wrow + 16 * ks);
-    acc[i] = f32x16{};
-#pragma unroll
-    for (int ks = 0; ks < DK; ++ks) acc[i] = mfma32x32x16(a[ks], bq[ks], acc[i]);
+    for (int ks = 0; ks < DK; ++ks) a[i][ks] = *(const bf16x8*)(wrow + 16 * ks);
   }
-  if (n >= N) return;
-  uint16_t* orow = q_lat + ((size_t)n * H + h) * R;
+  for (int nb = nb0; nb < nb0 + nbn && nb * 32 < N; ++nb) {
+    const int n = nb * 32 + l32;
+    const int nc = min(n, N - 1);
+    const uint16_t* qrow = q + ((size_t)nc * H + h) * d + 8 * g;
+    bf16x8 bq[DK];
 #pragma unroll
-  for (int i = 0; i < NB; ++i)
+    for (int ks = 0; ks < DK; ++ks) bq[ks] = *(const bf16x8*)(qrow + 16 * ks);
+    f32x16 acc[NB];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int rho = rho0 + 32 * i + 8 * j + 4 * g;
-      u32x2 v = {pack_bf16x2(acc[i][4 * j] * qscale, acc[i][4 * j + 1] * qscale),
-                 pack_bf16x2(acc[i][4 * j + 2] * qscale, acc[i][4 * j + 3] * qscale)};
-      *(u32x2*)(orow + rho) = v;
+    for (int i = 0; i < NB; ++i) {
+      acc[i] = f32x16{};
+#pragma unroll
+      for (int ks = 0; ks < DK; ++ks) acc[i] = mfma32x32x16(a[i][ks], bq[ks], acc[i]);
     }
+    if (n < N) {
+      uint16_t* orow = q_lat + ((size_t)n * H + h) * R;
+#pragma unroll
+      for (int i = 0; i < NB; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int rho = rho0 + 32 * i + 8 * j + 4 * g;
+          u32x2 v = {pack_bf16x2(acc[i][4 * j] * qscale, acc[i][4 * j + 1] * qscale),
+                     pack_bf16x2(acc[i][4 * j + 2] * qscale, acc[i][4 * j + 3] * qscale)};
+          *(u32x2*)(orow + rho) = v;
+        }
+    }
+  }
 }
 
 // W_uv [R, H, d] -> W_uv^T [H, d, R], so the up-projection reads rho-contiguous
