@@ -296,136 +296,115 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
-// Merge + up-projection.  Block (h, group of 16 sequences):
+// Merge + up-projection.  Block (h, group of 16 sequences), 16 waves:
 //   o_b = sum_i w_i o_i,  w_i = l_i 2^(m_i - m*) / sum_k l_k 2^(m_k - m*),  m* = max_i m_i
-// over the splits i of sequence b (o_i normalised), then
+// over the partial states i of sequence b (o_i normalised), then
 //   out[b, h, :] = o_b W_uv[:, h, :]   (16 x R times R x d on the matrix unit,
 //   W_uv^T [H][d][R] from the prologue).
-// Wave w merges sequences 4 w .. 4 w + 3.  Every phase issues all its loads
-// before using them, so each costs about one memory round trip: the split
-// weights (lanes over splits), the weighted sum (lane 16 k + c owns rho
-// [c R / 16, (c + 1) R / 16) of sequence 4 w + k), the up-projection operands.
+// Wave v merges sequence b0 + v with lane l owning rho [8 l, 8 l + 8) of
+// each 512-wide slice.  Every load of the block -- the partial states, their
+// (m, l) and the up-projection operands -- is issued at the start, so the
+// kernel costs about one memory round trip.
+constexpr int kMergePrefetch = 8;  // partial states of a sequence loaded up front
 template <int R>
-__global__ __launch_bounds__(256) void decode_merge_up(const uint16_t* __restrict__ part_o,
-                                                       const float* __restrict__ part_ml,
-                                                       const int32_t* __restrict__ S,
-                                                       const uint16_t* __restrict__ wvT,
-                                                       uint16_t* __restrict__ out, int B, int H, int d, int P) {
-  constexpr int NCH = R / 128;  // 16-byte chunks per lane in the weighted sum
+__global__ __launch_bounds__(1024) void decode_merge_up(const uint16_t* __restrict__ part_o,
+                                                        const float* __restrict__ part_ml,
+                                                        const int32_t* __restrict__ S,
+                                                        const uint16_t* __restrict__ wvT,
+                                                        uint16_t* __restrict__ out, int B, int H, int d, int P) {
   constexpr int NKS = R / 32;   // contraction steps of the up-projection
+  constexpr int NC = R / 512 > 0 ? R / 512 : 1;  // 8-wide rho chunks per lane
+  constexpr int LANES = R / (8 * NC);            // lanes that hold rho (R < 512: fewer)
   __shared__ __attribute__((aligned(16))) uint16_t ob[16][R + 8];
-  __shared__ float wts[4][4][64];  // [wave][sequence][split within a chunk of 64]
   const int h = blockIdx.x, b0 = blockIdx.y * 16;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int v = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int G = lane >> 4, n = lane & 15;
   const int neb = d / 16;
 
-  // up-projection operands of this wave's first output block, in flight early
+  // up-projection operands of this wave's output block
   bf16x8 wa[NKS];
-  if (w < neb) {
-    const uint16_t* wrow = wvT + ((size_t)h * d + 16 * w + n) * R + 8 * G;
+  if (v < neb) {
+    const uint16_t* wrow = wvT + ((size_t)h * d + 16 * v + n) * R + 8 * G;
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) wa[ks] = *(const bf16x8*)(wrow + 32 * ks);
   }
-
   // partial slots of sequence b: g + b for the chunks g that hold its keys
-  const int C = decode_chunk(S[B], P);
-  auto slots = [&](int b) {
-    if (b >= B) return int2{0, 0};
+  const int b = b0 + v;
+  int base = 0, cnt = 0;
+  if (b < B) {
+    const int C = decode_chunk(S[B], P);
     const int sb = S[b], se = S[b + 1];
     const int g0 = sb / C, g1 = (se - 1) / C;
-    return int2{g0 + b, g1 - g0 + 1};
-  };
-  int2 si[4];
-#pragma unroll
-  for (int k = 0; k < 4; ++k) si[k] = slots(b0 + 4 * w + k);
-  // (m, l) of the first 64 splits of each sequence in registers, lane = split
-  float2 ml0[4];
-#pragma unroll
-  for (int k = 0; k < 4; ++k)
-    ml0[k] = lane < si[k].y ? *(const float2*)(part_ml + ((size_t)(si[k].x + lane) * H + h) * 2)
-                            : float2{-INFINITY, 0.f};
-  float mx[4], inv[4];
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    float m = ml0[k].x;
-    for (int j = lane + 64; j < si[k].y; j += 64) m = fmaxf(m, part_ml[((size_t)(si[k].x + j) * H + h) * 2]);
-    mx[k] = wave_max(m);
+    base = g0 + b;
+    cnt = g1 - g0 + 1;
   }
+  base = __builtin_amdgcn_readfirstlane(base);
+  cnt = __builtin_amdgcn_readfirstlane(cnt);
+  // partial states 0 .. kMergePrefetch - 1 and the (m, l) of splits lane, lane + 64, ...
+  u32x4 po[kMergePrefetch][NC];
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    float ls = lane < si[k].y ? ml0[k].y * exp2f(ml0[k].x - mx[k]) : 0.f;
-    for (int j = lane + 64; j < si[k].y; j += 64) {
-      const float2 ml = *(const float2*)(part_ml + ((size_t)(si[k].x + j) * H + h) * 2);
-      ls += ml.y * exp2f(ml.x - mx[k]);
-    }
-    ls = wave_sum(ls);
-    inv[k] = ls > 0.f ? 1.f / ls : 0.f;
+  for (int j = 0; j < kMergePrefetch; ++j)
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+      po[j][c] = j < cnt && lane < LANES
+                     ? *(const u32x4*)(part_o + ((size_t)(base + j) * H + h) * R + 8 * (lane + 64 * c))
+                     : u32x4{0, 0, 0, 0};
+  float2 ml0 = lane < cnt ? *(const float2*)(part_ml + ((size_t)(base + lane) * H + h) * 2) : float2{-INFINITY, 0.f};
+  float m = ml0.x;
+  for (int j = lane + 64; j < cnt; j += 64) m = fmaxf(m, part_ml[((size_t)(base + j) * H + h) * 2]);
+  m = wave_max(m);
+  float ls = lane < cnt ? ml0.y * exp2f(ml0.x - m) : 0.f;
+  for (int j = lane + 64; j < cnt; j += 64) {
+    const float2 ml = *(const float2*)(part_ml + ((size_t)(base + j) * H + h) * 2);
+    ls += ml.y * exp2f(ml.x - m);
   }
-
-  // weighted sum, in chunks of 64 splits
-  const int kq = G, c = n;
-  const int2 mys = slots(b0 + 4 * w + kq);
-  int maxc = si[0].y;
+  ls = wave_sum(ls);
+  const float inv = ls > 0.f ? 1.f / ls : 0.f;
+  const float wl = lane < cnt ? ml0.y * exp2f(ml0.x - m) * inv : 0.f;  // weight of split `lane`
+  float acc[8 * NC];
 #pragma unroll
-  for (int k = 1; k < 4; ++k) maxc = max(maxc, si[k].y);
-  float acc[8 * NCH];
+  for (int i = 0; i < 8 * NC; ++i) acc[i] = 0.f;
+  auto add = [&](float wt, const u32x4 (&x)[NC]) {
 #pragma unroll
-  for (int i = 0; i < 8 * NCH; ++i) acc[i] = 0.f;
-  for (int c0 = 0; c0 < maxc; c0 += 64) {
+    for (int c = 0; c < NC; ++c)
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      float2 ml = ml0[k];
-      if (c0 > 0)
-        ml = c0 + lane < si[k].y ? *(const float2*)(part_ml + ((size_t)(si[k].x + c0 + lane) * H + h) * 2)
-                                 : float2{-INFINITY, 0.f};
-      wts[w][k][lane] = c0 + lane < si[k].y ? ml.y * exp2f(ml.x - mx[k]) * inv[k] : 0.f;
-    }
-    const int nj = min(64, maxc - c0);
-#pragma unroll 4
-    for (int jj = 0; jj < nj; ++jj) {
-      if (c0 + jj < mys.y) {
-        const float wt = wts[w][kq][jj];
-        const uint16_t* src = part_o + ((size_t)(mys.x + c0 + jj) * H + h) * R + c * (R / 16);
-#pragma unroll
-        for (int i = 0; i < NCH; ++i) {
-          const u32x4 v = *(const u32x4*)(src + 8 * i);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            acc[8 * i + 2 * e] += wt * __uint_as_float(v[e] << 16);
-            acc[8 * i + 2 * e + 1] += wt * __uint_as_float(v[e] & 0xFFFF0000u);
-          }
-        }
+      for (int e = 0; e < 4; ++e) {
+        acc[8 * c + 2 * e] += wt * __uint_as_float(x[c][e] << 16);
+        acc[8 * c + 2 * e + 1] += wt * __uint_as_float(x[c][e] & 0xFFFF0000u);
       }
-    }
-  }
+  };
 #pragma unroll
-  for (int i = 0; i < NCH; ++i) {
-    const u32x4 r = {pack_bf16x2(acc[8 * i], acc[8 * i + 1]), pack_bf16x2(acc[8 * i + 2], acc[8 * i + 3]),
-                     pack_bf16x2(acc[8 * i + 4], acc[8 * i + 5]), pack_bf16x2(acc[8 * i + 6], acc[8 * i + 7])};
-    *(u32x4*)&ob[4 * w + kq][c * (R / 16) + 8 * i] = r;
+  for (int j = 0; j < kMergePrefetch; ++j)
+    if (j < cnt) add(__shfl(wl, j), po[j]);
+  for (int j = kMergePrefetch; j < cnt; ++j) {  // rare: more partial states than prefetched
+    const float2 ml = *(const float2*)(part_ml + ((size_t)(base + j) * H + h) * 2);
+    u32x4 x[NC];
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+      x[c] = lane < LANES ? *(const u32x4*)(part_o + ((size_t)(base + j) * H + h) * R + 8 * (lane + 64 * c))
+                          : u32x4{0, 0, 0, 0};
+    add(ml.y * exp2f(ml.x - m) * inv, x);
   }
+  if (lane < LANES)
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+      *(u32x4*)&ob[v][8 * (lane + 64 * c)] =
+          u32x4{pack_bf16x2(acc[8 * c], acc[8 * c + 1]), pack_bf16x2(acc[8 * c + 2], acc[8 * c + 3]),
+                pack_bf16x2(acc[8 * c + 4], acc[8 * c + 5]), pack_bf16x2(acc[8 * c + 6], acc[8 * c + 7])};
   __syncthreads();
-
   // out^T[e][b] = sum_rho W_uv^T[e][rho] o[b][rho]: A = W_uv^T (e rows), B = o^T
-  for (int eb = w; eb < neb; eb += 4) {
-    if (eb != w) {
-      const uint16_t* wrow = wvT + ((size_t)h * d + 16 * eb + n) * R + 8 * G;
-#pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) wa[ks] = *(const bf16x8*)(wrow + 32 * ks);
-    }
+  if (v < neb) {
     f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < NKS; ks += 2) {
       a0 = mfma16x16x32(wa[ks], *(const bf16x8*)&ob[n][32 * ks + 8 * G], a0);
       a1 = mfma16x16x32(wa[ks + 1], *(const bf16x8*)&ob[n][32 * ks + 32 + 8 * G], a1);
     }
-    // (a0 + a1)[v] = out^T[e = 16 eb + 4 G + v][b = b0 + n]
-    const int b = b0 + n;
-    if (b < B) {
-      uint16_t* dst = out + ((size_t)b * H + h) * d + 16 * eb + 4 * G;
-      const u32x2 v = {pack_bf16x2(a0[0] + a1[0], a0[1] + a1[1]), pack_bf16x2(a0[2] + a1[2], a0[3] + a1[3])};
-      *(u32x2*)dst = v;
+    // (a0 + a1)[u] = out^T[e = 16 v + 4 G + u][b = b0 + n]
+    if (b0 + n < B) {
+      uint16_t* dst = out + ((size_t)(b0 + n) * H + h) * d + 16 * v + 4 * G;
+      *(u32x2*)dst = u32x2{pack_bf16x2(a0[0] + a1[0], a0[1] + a1[1]), pack_bf16x2(a0[2] + a1[2], a0[3] + a1[3])};
     }
   }
 }
@@ -485,7 +464,7 @@ static hipError_t run_decode(const uint16_t* q, const uint16_t* lat, const int32
   }
   {
     ProfScope ps("decode_merge_up", st);
-    hipLaunchKernelGGL(decode_merge_up<R>, dim3(H, (B + 15) / 16), dim3(256), 0, st, part_o, part_ml, S, wvT, out,
+    hipLaunchKernelGGL(decode_merge_up<R>, dim3(H, (B + 15) / 16), dim3(1024), 0, st, part_o, part_ml, S, wvT, out,
                        B, H, d, P);
   }
   return hipGetLastError();
