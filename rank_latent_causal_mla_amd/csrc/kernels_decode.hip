@@ -264,7 +264,7 @@ void decode_split(const uint16_t* __restrict__ q_lat, const uint16_t* __restrict
 // Prologue of a decode call in one launch (independent block roles):
 //   block 0                  -- the prefix S of the clamped lengths;
 //   the next nabs blocks     -- absorption, 32 sequences x 128 rho of one head each;
-//   the last ntr blocks      -- the W_uv transpose, 32 x 32 tiles.
+//   the last ntr blocks      -- the W_uv transpose, 64 x 64 tiles.
 template <int R, int DK>
 __global__ __launch_bounds__(256) void decode_prep(const uint16_t* __restrict__ q, const uint16_t* __restrict__ wk,
                                                    uint16_t* __restrict__ q_lat, const uint16_t* __restrict__ wv,
@@ -280,7 +280,7 @@ __global__ __launch_bounds__(256) void decode_prep(const uint16_t* __restrict__ 
     absorb_tile<R, DK, 1>(q, wk, q_lat, B, H, qscale, t / (H * NQ), 1, (t / NQ) % H, 128 * (t % NQ));
   } else {
     const int t = bid - 1 - nabs;
-    const int nrb = R / 32, neb = (d + 31) / 32;
+    const int nrb = R / kTransposeTile, neb = (d + kTransposeTile - 1) / kTransposeTile;
     transpose_wv_tile(wv, wvT, R, H, d, t % nrb, (t / nrb) % neb, t / (nrb * neb));
   }
 }
@@ -443,7 +443,7 @@ static hipError_t run_decode(const uint16_t* q, const uint16_t* lat, const int32
   {
     ProfScope ps("decode_prep", st);
     const int nabs = ((B + 31) / 32) * H * (R / 128);
-    const int ntr = (R / 32) * ((d + 31) / 32) * H;
+    const int ntr = (R / kTransposeTile) * ((d + kTransposeTile - 1) / kTransposeTile) * H;
     const dim3 grid(1 + nabs + ntr);
 #define PREP(DK)                                                                                          \
   hipLaunchKernelGGL((decode_prep<R, DK>), grid, dim3(256), 0, st, q, wk, q_lat, wv, wvT, lens, B, Tmax, H, d, \

@@ -68,7 +68,8 @@ hipError_t absorb_mfma(const uint16_t* q, const uint16_t* wk, uint16_t* q_lat, i
 }
 
 hipError_t transpose_wv_launch(const uint16_t* wv, uint16_t* wvT, int R, int H, int d, hipStream_t st) {
-  hipLaunchKernelGGL(transpose_wv, dim3((R + 31) / 32, (d + 31) / 32, H), dim3(256), 0, st, wv, wvT, R, H, d);
+  hipLaunchKernelGGL(transpose_wv, dim3(R / kTransposeTile, (d + kTransposeTile - 1) / kTransposeTile, H), dim3(256), 0, st,
+                     wv, wvT, R, H, d);
   return hipGetLastError();
 }
 

@@ -61,20 +61,36 @@ __device__ __forceinline__ void absorb_tile(const uint16_t* __restrict__ q, cons
 }
 
 // W_uv [R, H, d] -> W_uv^T [H, d, R], so the up-projection reads rho-contiguous
-// rows.  The block transposes the 32 x 32 tile (rho block rb, e block eb) of head h.
+// rows.  The block transposes the 64 x 64 tile (rho block rb, e block eb) of
+// head h through LDS, reading and writing 16-byte pieces (d and R are
+// multiples of 32 and 64 on this path; e past d is skipped).
+constexpr int kTransposeTile = 64;
 __device__ __forceinline__ void transpose_wv_tile(const uint16_t* __restrict__ wv, uint16_t* __restrict__ wvT,
                                                   int R, int H, int d, int rb, int eb, int h) {
-  __shared__ uint16_t tile[32][33];
-  const int rho0 = rb * 32, e0 = eb * 32;
-  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;  // 32 x 8 threads
-  for (int k = ty; k < 32; k += 8) {
-    const int rho = rho0 + k, e = e0 + tx;
-    tile[k][tx] = (rho < R && e < d) ? wv[((size_t)rho * H + h) * d + e] : 0;
+  __shared__ __attribute__((aligned(16))) uint16_t tile[64][64 + 8];
+  const int rho0 = rb * 64, e0 = eb * 64;
+  const int tid = threadIdx.x;
+  // read: 64 rho rows x 8 pieces of 8 e
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int idx = tid + 256 * k, r = idx >> 3, c = idx & 7;
+    const int e = e0 + 8 * c;
+    u32x4 v = {0, 0, 0, 0};
+    if (e < d) v = *(const u32x4*)(wv + ((size_t)(rho0 + r) * H + h) * d + e);
+    *(u32x4*)&tile[r][8 * c] = v;
   }
   __syncthreads();
-  for (int k = ty; k < 32; k += 8) {
-    const int e = e0 + k, rho = rho0 + tx;
-    if (e < d && rho < R) wvT[((size_t)h * d + e) * R + rho] = tile[tx][k];
+  // write: 64 e rows x 8 pieces of 8 rho
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int idx = tid + 256 * k, er = idx >> 3, c = idx & 7;
+    const int e = e0 + er;
+    if (e >= d) continue;
+    uint32_t w4[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      w4[i] = (uint32_t)tile[8 * c + 2 * i][er] | ((uint32_t)tile[8 * c + 2 * i + 1][er] << 16);
+    *(u32x4*)(wvT + ((size_t)h * d + e) * R + rho0 + 8 * c) = u32x4{w4[0], w4[1], w4[2], w4[3]};
   }
 }
 
