@@ -75,41 +75,81 @@ hipError_t transpose_wv_launch(const uint16_t* wv, uint16_t* wvT, int R, int H, 
 
 // ---------------------------------------------------------------------------
 // Up-projection: out[n, h, e] = sum_rho o_lat[n*H + h, rho] * W_uv[rho, h, e],
-// computed as out^T = W_uv^T o_lat^T.  Block: head h, row blocks
-// kUpRowBlocks * blockIdx.x .. of 32 rows; wave w takes the output blocks
-// e = 32 i .. 32 i + 31 for i = w, w + 4, ..., holding that slice of W_uv^T
-// in registers across the row blocks, so W_uv is read once per block.
+// computed as out^T = W_uv^T o_lat^T.  Block: head h, output columns
+// e = 128 blockIdx.z + 32 w .. (wave w holds that slice of W_uv^T in
+// registers), and row blocks kUpRowBlocks * blockIdx.x .. of 32 rows.  The
+// o_lat rows of a row block are copied once per block into LDS by LDS-DMA
+// (two buffers, the next block's copy in flight), chunk-swizzled by the row
+// so the four waves' operand reads are conflict-free.
 constexpr int kUpRowBlocks = 8;
+template <int R>
+constexpr size_t up_lds_bytes() { return (size_t)2 * 32 * R * 2; }
+
 template <int R>
 __global__ __launch_bounds__(256, 2) void up_bf16(const uint16_t* __restrict__ o_lat,
                                                   const uint16_t* __restrict__ wvT,
                                                   uint16_t* __restrict__ out, int N, int H, int d) {
-  constexpr int NKS = R / 16;  // contraction steps
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  constexpr int NKS = R / 16;           // contraction steps
+  constexpr int TB = 32 * R * 2;        // one row block in LDS
+  constexpr int NC = R / 8;             // 16-byte chunks per row
+  constexpr int RPI = 64 / NC;          // rows per copy instruction
+  constexpr int NI = TB / 1024 / 4;     // copy instructions per wave and row block
+  static_assert(NC <= 64 && 64 % NC == 0, "a copy instruction covers whole rows");
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane >> 5, l32 = lane & 31;
   const int h = blockIdx.y;
-  const int neb = d / 32;
+  const int i = 4 * blockIdx.z + w;  // output block of 32 columns
+  const bool has_cols = i < d / 32;
   const int nb0 = blockIdx.x * kUpRowBlocks;
-  for (int i = w; i < neb; i += 4) {
-    bf16x8 a[NKS];
+  const int nrb_all = (N + 31) / 32;
+  const int nbn = nrb_all - nb0 < kUpRowBlocks ? nrb_all - nb0 : kUpRowBlocks;
+  const uint32_t lds0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)smem);
+
+  bf16x8 a[NKS];
+  if (has_cols) {
     const uint16_t* wrow = wvT + ((size_t)h * d + 32 * i + l32) * R + 8 * g;
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) a[ks] = *(const bf16x8*)(wrow + 16 * ks);
-    for (int nb = nb0; nb < nb0 + kUpRowBlocks && nb * 32 < N; ++nb) {
-      const int n = nb * 32 + l32;
-      const uint16_t* orow = o_lat + ((size_t)min(n, N - 1) * H + h) * R + 8 * g;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) asm volatile("" : : "v"(a[ks]));  // loaded before the copies start
+  }
+  // copy of row block k (rows 32 (nb0 + k) + s, s = 0..31) into buffer k & 1
+  const int sl = lane / NC, p = lane % NC;
+  auto copy = [&](int k) {
+#pragma unroll
+    for (int u = 0; u < NI; ++u) {
+      const int ins = 4 * u + w;
+      const int s = ins * RPI + sl;  // row within the block
+      const int n = min(32 * (nb0 + k) + s, N - 1);
+      const int n0 = __builtin_amdgcn_readfirstlane(min(32 * (nb0 + k) + ins * RPI, N - 1));
+      const int c = (p & ~15) | ((p & 15) ^ (s & 15));
+      dma16(o_lat + ((size_t)n0 * H + h) * R, (uint32_t)(((size_t)(n - n0) * H) * R * 2 + 16 * c),
+            lds0 + (k & 1) * TB + ins * 1024);
+    }
+  };
+  copy(0);
+  for (int k = 0; k < nbn; ++k) {
+    if (k + 1 < nbn) {
+      copy(k + 1);
+      dma_wait<NI>();  // own part of row block k landed
+    } else {
+      dma_wait<0>();
+    }
+    __builtin_amdgcn_s_barrier();
+    if (has_cols) {
+      const char* buf = smem + (k & 1) * TB + l32 * (R * 2);
       f32x16 acc0 = f32x16{}, acc1 = f32x16{};
 #pragma unroll
-      for (int k8 = 0; k8 < NKS; k8 += 8) {  // eight operand loads ahead of their matrix ops
-        bf16x8 bo[8];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) bo[u] = *(const bf16x8*)(orow + 16 * (k8 + u));
-#pragma unroll
-        for (int u = 0; u < 8; u += 2) {
-          acc0 = mfma32x32x16(a[k8 + u], bo[u], acc0);
-          acc1 = mfma32x32x16(a[k8 + u + 1], bo[u + 1], acc1);
-        }
+      for (int ks = 0; ks < NKS; ks += 2) {
+        const int c0 = 2 * ks + g, c1 = c0 + 2;
+        const bf16x8 b0 = lds_read16(buf + 16 * ((c0 & ~15) | ((c0 & 15) ^ (l32 & 15))));
+        const bf16x8 b1 = lds_read16(buf + 16 * ((c1 & ~15) | ((c1 & 15) ^ (l32 & 15))));
+        acc0 = mfma32x32x16(a[ks], b0, acc0);
+        acc1 = mfma32x32x16(a[ks + 1], b1, acc1);
       }
+      const int n = 32 * (nb0 + k) + l32;
       if (n < N) {
         uint16_t* dst = out + ((size_t)n * H + h) * d;
 #pragma unroll
@@ -121,6 +161,7 @@ __global__ __launch_bounds__(256, 2) void up_bf16(const uint16_t* __restrict__ o
         }
       }
     }
+    __builtin_amdgcn_s_barrier();  // buffer k & 1 is refilled next iteration
   }
 }
 
@@ -399,6 +440,9 @@ static hipError_t run_prefill(const uint16_t* q, const uint16_t* lat, const uint
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute((const void*)flash_latent_bf16<R>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)flash_lds_bytes(R));
+    if (e == hipSuccess)
+      e = hipFuncSetAttribute((const void*)up_bf16<R>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                              (int)up_lds_bytes<R>());
     if (e != hipSuccess) return e;
     attr_set = true;
   }
@@ -418,8 +462,8 @@ static hipError_t run_prefill(const uint16_t* q, const uint16_t* lat, const uint
   }
   {
     ProfScope ps("up_bf16", st);
-    hipLaunchKernelGGL(up_bf16<R>, dim3((N + 32 * kUpRowBlocks - 1) / (32 * kUpRowBlocks), H), dim3(256), 0, st, o_lat,
-                       wvT, out, N, H, d);
+    hipLaunchKernelGGL(up_bf16<R>, dim3((N + 32 * kUpRowBlocks - 1) / (32 * kUpRowBlocks), H, (d + 127) / 128),
+                       dim3(256), up_lds_bytes<R>(), st, o_lat, wvT, out, N, H, d);
   }
   return hipGetLastError();
 }
