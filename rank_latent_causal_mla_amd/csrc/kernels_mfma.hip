@@ -22,10 +22,26 @@ namespace mla {
 // ---------------------------------------------------------------------------
 // Absorption (one block per 32 query rows of one head, the whole rank) and
 // the W_uv transpose, as kernels around the block bodies of prep_blocks.h.
-// Row blocks of 32 rows per absorption block, and the rank slice per block.
+// Absorption for prefill: q_lat[n*H + h, rho] = qscale * sum_e W_uk[rho, h, e] * q[n, h, e]
+// (n = b*T + t; qscale folds the softmax scale and log2 e into q_lat).
+// Computed transposed, q_lat^T = W_h q_h^T.  Block: head h, the rank slice
+// [128 NB blockIdx.z, +128 NB) (wave w holds its 32 NB rows of W_uk in
+// registers) and kAbsorbRowBlocks row blocks of 32 queries, whose q rows are
+// copied into LDS once per block by LDS-DMA (two buffers, the next copy in
+// flight), chunk-swizzled so the operand reads are conflict-free.
 constexpr int kAbsorbRowBlocks = 8;
 template <int R, int DK>
 constexpr int absorb_nb() { return R / 128 < 32 / DK ? R / 128 : 32 / DK; }
+
+// 16-byte chunk c of q row s (d / 8 chunks per row) sits at position
+// qswz(c, s): within every 256 bytes of LDS, 16 consecutive rows reading the
+// same chunk hit 16 distinct slots.
+template <int DK>
+__device__ __forceinline__ int qswz(int c, int s) {
+  constexpr int NCd = 2 * DK;  // chunks per row
+  if constexpr (NCd >= 16) return (c & ~15) | ((c & 15) ^ (s & 15));
+  else return c ^ ((s / (16 / NCd)) & (NCd - 1));
+}
 
 template <int R, int DK>
 __global__ __launch_bounds__(256, 2) void absorb_bf16(const uint16_t* __restrict__ q,
@@ -33,8 +49,85 @@ __global__ __launch_bounds__(256, 2) void absorb_bf16(const uint16_t* __restrict
                                                       uint16_t* __restrict__ q_lat, int N, int H,
                                                       float qscale) {
   constexpr int NB = absorb_nb<R, DK>();
-  absorb_tile<R, DK, NB>(q, wk, q_lat, N, H, qscale, blockIdx.x * kAbsorbRowBlocks, kAbsorbRowBlocks, blockIdx.y,
-                         128 * NB * blockIdx.z);
+  constexpr int d = 16 * DK;
+  constexpr int TB = 32 * d * 2;                      // q rows of one row block
+  constexpr int NCd = d / 8;                          // chunks per row
+  constexpr int RPI = 64 / NCd;                       // rows per copy instruction
+  constexpr int NINS = TB / 1024;                     // copy instructions per row block
+  constexpr int NIW = NINS >= 4 ? NINS / 4 : 1;       // at most, per wave
+  static_assert(NCd <= 64 && 64 % NCd == 0 && TB % 1024 == 0, "copies cover whole rows");
+  __shared__ __attribute__((aligned(16))) char buf[2][TB];
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int g = lane >> 5, l32 = lane & 31;
+  const int h = blockIdx.y;
+  const int rho0 = 128 * NB * blockIdx.z + w * 32 * NB;
+  const int nb0 = blockIdx.x * kAbsorbRowBlocks;
+  const int nrb_all = (N + 31) / 32;
+  const int nbn = nrb_all - nb0 < kAbsorbRowBlocks ? nrb_all - nb0 : kAbsorbRowBlocks;
+  const uint32_t lds0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)&buf[0][0]);
+
+  bf16x8 a[NB][DK];
+#pragma unroll
+  for (int i = 0; i < NB; ++i) {
+    const uint16_t* wrow = wk + ((size_t)(rho0 + 32 * i + l32) * H + h) * d + 8 * g;
+#pragma unroll
+    for (int ks = 0; ks < DK; ++ks) a[i][ks] = *(const bf16x8*)(wrow + 16 * ks);
+  }
+#pragma unroll
+  for (int i = 0; i < NB; ++i)
+#pragma unroll
+    for (int ks = 0; ks < DK; ++ks) asm volatile("" : : "v"(a[i][ks]));  // loaded before the copies start
+  const int sl = lane / NCd, p = lane % NCd;
+  auto copy = [&](int k) {
+#pragma unroll
+    for (int u = 0; u < NIW; ++u) {
+      const int ins = 4 * u + w;
+      if (ins < NINS) {
+        const int s = ins * RPI + sl;  // row within the block
+        const int n = min(32 * (nb0 + k) + s, N - 1);
+        const int n0 = __builtin_amdgcn_readfirstlane(min(32 * (nb0 + k) + ins * RPI, N - 1));
+        const int c = qswz<DK>(p, s);  // the swizzle is its own inverse
+        dma16(q + ((size_t)n0 * H + h) * d, (uint32_t)(((size_t)(n - n0) * H) * d * 2 + 16 * c),
+              lds0 + (k & 1) * TB + ins * 1024);
+      }
+    }
+  };
+  copy(0);
+  for (int k = 0; k < nbn; ++k) {
+    if (k + 1 < nbn) {
+      copy(k + 1);
+      dma_wait<NIW>();  // own part of row block k landed
+    } else {
+      dma_wait<0>();
+    }
+    __builtin_amdgcn_s_barrier();
+    const char* row = &buf[k & 1][0] + l32 * (d * 2);
+    bf16x8 bq[DK];
+#pragma unroll
+    for (int ks = 0; ks < DK; ++ks) bq[ks] = lds_read16(row + 16 * qswz<DK>(2 * ks + g, l32));
+    f32x16 acc[NB];
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      acc[i] = f32x16{};
+#pragma unroll
+      for (int ks = 0; ks < DK; ++ks) acc[i] = mfma32x32x16(a[i][ks], bq[ks], acc[i]);
+    }
+    const int n = 32 * (nb0 + k) + l32;
+    if (n < N) {
+      uint16_t* orow = q_lat + ((size_t)n * H + h) * R;
+#pragma unroll
+      for (int i = 0; i < NB; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int rho = rho0 + 32 * i + 8 * j + 4 * g;
+          u32x2 v = {pack_bf16x2(acc[i][4 * j] * qscale, acc[i][4 * j + 1] * qscale),
+                     pack_bf16x2(acc[i][4 * j + 2] * qscale, acc[i][4 * j + 3] * qscale)};
+          *(u32x2*)(orow + rho) = v;
+        }
+    }
+    __builtin_amdgcn_s_barrier();  // buffer k & 1 is refilled next iteration
+  }
 }
 
 __global__ __launch_bounds__(256) void transpose_wv(const uint16_t* __restrict__ wv, uint16_t* __restrict__ wvT,
