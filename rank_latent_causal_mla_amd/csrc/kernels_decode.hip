@@ -58,49 +58,93 @@ __device__ __forceinline__ int decode_chunk(int N, int P) {
 }
 
 template <int R>
-__device__ __forceinline__ void decode_segment(const uint16_t* __restrict__ q_lat,
-                                               const uint16_t* __restrict__ lat, uint16_t* __restrict__ part_o,
-                                               float* __restrict__ part_ml, int Tmax, int H, int hg, int b,
-                                               int k0, int k1, int slot) {
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
+void decode_split(const uint16_t* __restrict__ q_lat, const uint16_t* __restrict__ lat,
+                  const int32_t* __restrict__ S, uint16_t* __restrict__ part_o,
+                  float* __restrict__ part_ml, int B, int Tmax, int H, int P) {
   constexpr int TILE = kDecodeTileKeys * R * 2;
-  constexpr int NKS = R / 32;       // contraction steps of a score block
-  constexpr int NCW = R / 64;       // 16-column blocks of this wave's quarter
   constexpr int NI = TILE / 1024 / 4;  // copy instructions per wave and tile
+  constexpr int NKS = R / 32;          // contraction steps of a score block
+  constexpr int NCW = R / 64;          // 16-column blocks of this wave's quarter
   static_assert(kDecodeBufs == 4, "dma_wait_tiles covers up to 2 later tiles");
   static_assert(NKS % 2 == 0, "two score chains");
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  // after the ring: P [2 q][4 G][16 n][2 kb][4] bf16, maxima [2 kb][2 q][16] f32
+  // after the ring: P [2 q][4 G][16 n][2 kb][4] bf16, maxima [2 kb][2 q][16] f32, l likewise
   char* pbuf = smem + kDecodeBufs * TILE;
   float* mxbuf = (float*)(pbuf + 2048);
+  float* lbuf = mxbuf + 64;
+  __shared__ int first_seq;
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int kb = w >> 1, qb = w & 1;
   const int G = lane >> 4, n = lane & 15;
-  const int ntile = (k1 - k0 + kDecodeTileKeys - 1) / kDecodeTileKeys;
-  const uint16_t* latb = lat + (size_t)b * Tmax * R;
+  const int g = blockIdx.x, hg = blockIdx.y;
+  const int N = S[B];
+  const int C = decode_chunk(N, P);
+  const int x0 = (int)min((long long)g * C, (long long)N);
+  const int x1 = (int)min((long long)x0 + C, (long long)N);
+  if (x0 >= x1) return;  // whole block: chunk past the end
+  // sequence holding key x0 (S is nondecreasing with positive steps)
+  for (int i = tid; i < B; i += 256)
+    if (S[i] <= x0 && x0 < S[i + 1]) first_seq = i;
+  __syncthreads();
+  const int b_first = __builtin_amdgcn_readfirstlane(first_seq);
   const uint32_t lds0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)smem);
+  // end of sequence b's part of the chunk, in its own key positions
+  auto seg_end = [&](int b) {
+    const int sb = __builtin_amdgcn_readfirstlane(S[b]), se = __builtin_amdgcn_readfirstlane(S[b + 1]);
+    return (x1 < se ? x1 : se) - sb;
+  };
+  auto seg_more = [&](int b) { return b < B && __builtin_amdgcn_readfirstlane(S[b]) < x1; };
+  const int k_first = x0 - __builtin_amdgcn_readfirstlane(S[b_first]);
 
-  // first tiles in flight while the queries load
+  // The chunk as one stream of 32-key tiles, segment after segment; the copy
+  // cursor runs three tiles ahead of the compute cursor, across segments.
+  int db = b_first, dk = k_first, dend = seg_end(b_first);
+  bool ddone = false;
+  int issued = 0;
+  auto copy_next = [&]() {
+    dma_tile32<R>(lat + (size_t)db * Tmax * R, dk, dend, lds0 + (issued % kDecodeBufs) * TILE, w);
+    ++issued;
+    dk += kDecodeTileKeys;
+    if (dk >= dend) {
+      ++db;
+      if (seg_more(db)) {
+        dk = 0;
+        dend = seg_end(db);
+      } else {
+        ddone = true;
+      }
+    }
+  };
 #pragma unroll
   for (int t = 0; t < kDecodeBufs - 1; ++t)
-    if (t < ntile) dma_tile32<R>(latb, k0 + kDecodeTileKeys * t, k1, lds0 + t * TILE, w);
+    if (!ddone) copy_next();
+
+  int cb = b_first, ck = k_first, cend = seg_end(b_first);  // compute cursor
   bf16x8 qf[NKS];
-  {
+  auto load_q = [&](int b) {
     const int hh = hg * 32 + 16 * qb + n;
     const uint16_t* qrow = q_lat + ((size_t)b * H + (hh < H ? hh : H - 1)) * R + 8 * G;
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) qf[ks] = *(const bf16x8*)(qrow + 32 * ks);
-  }
-  // Consume the query registers before the loop: the copies are invisible
-  // to the compiler's wait counting, and a query load still pending at the
-  // loop head would make it wait on the vector-memory counter every iteration.
+    // Consume the query registers here: the copies are invisible to the
+    // compiler's wait counting, and a query load still pending in the loop
+    // would make it wait on the vector-memory counter every iteration.
 #pragma unroll
-  for (int ks = 0; ks < NKS; ++ks) asm volatile("" : : "v"(qf[ks]));
+    for (int ks = 0; ks < NKS; ++ks) asm volatile("" : : "v"(qf[ks]));
+  };
+  load_q(cb);
 
   f32x4 o[NCW][2];
+  float m_run[2], l_part;
+  auto reset = [&]() {
 #pragma unroll
-  for (int c = 0; c < NCW; ++c) o[c][0] = o[c][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run[2] = {-INFINITY, -INFINITY}, l_part = 0.f;
+    for (int c = 0; c < NCW; ++c) o[c][0] = o[c][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    m_run[0] = m_run[1] = -INFINITY;
+    l_part = 0.f;
+  };
+  reset();
   const int rw = w * (R / 4);
 
   // per-lane LDS offsets: score row 16 kb + n, transpose key 4 G + n / 4 (+16 t)
@@ -111,13 +155,42 @@ __device__ __forceinline__ void decode_segment(const uint16_t* __restrict__ q_la
   const int trh = (n & 3) >> 1;
   char* pw = pbuf + ((qb * 4 + G) * 16 + n) * 16 + kb * 8;  // this lane's 4 probabilities
 
-  if (ntile > 0) {
-    dma_wait_tiles<NI>(ntile - 1 < kDecodeBufs - 2 ? ntile - 1 : kDecodeBufs - 2);
-    __builtin_amdgcn_s_barrier();  // tile 0 landed for every wave
-  }
-  for (int j = 0; j < ntile; ++j) {
-    const char* tile = smem + (j % kDecodeBufs) * TILE;
-    const int kt = k0 + kDecodeTileKeys * j;
+  // partial state of sequence b's segment into slot g + b: l of every head
+  // from the two key halves (through LDS), o normalised, (m, l)
+  auto flush = [&](int b) {
+    float lsum = l_part + __shfl_xor(l_part, 16);
+    lsum += __shfl_xor(lsum, 32);
+    if (G == 0) lbuf[(kb * 2 + qb) * 16 + n] = lsum;
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    mfma_agpr_wait();
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const float lt = lbuf[q * 16 + n] + lbuf[(2 + q) * 16 + n];
+      const int hh = hg * 32 + 16 * q + n;
+      if (hh >= H) continue;
+      const float inv = 1.f / lt;
+      const size_t prow = (size_t)(g + b) * H + hh;
+      uint16_t* po = part_o + prow * R + rw + 4 * G;
+#pragma unroll
+      for (int c = 0; c < NCW; ++c) {
+        mfma_agpr_tie(o[c][q]);
+        const u32x2 v = {pack_bf16x2(o[c][q][0] * inv, o[c][q][1] * inv),
+                         pack_bf16x2(o[c][q][2] * inv, o[c][q][3] * inv)};
+        *(u32x2*)(po + 16 * c) = v;
+      }
+      if (w == 0 && G == 0) {
+        part_ml[prow * 2] = m_run[q];
+        part_ml[prow * 2 + 1] = lt;
+      }
+    }
+  };
+
+  dma_wait_tiles<NI>(issued - 1);  // tile 0 landed
+  __builtin_amdgcn_s_barrier();
+  for (int tau = 0;; ++tau) {
+    const char* tile = smem + (tau % kDecodeBufs) * TILE;
+    const int kt = ck;
 
     // ---- scores of this wave's block, two interleaved chains
     f32x4 sc0 = {0.f, 0.f, 0.f, 0.f}, sc1 = {0.f, 0.f, 0.f, 0.f};
@@ -132,8 +205,8 @@ __device__ __forceinline__ void decode_segment(const uint16_t* __restrict__ q_la
         sc1 = mfma16x16x32(a1, qf[ks + 1], sc1);
       }
     }
-    // keys >= k1 masked: key 16 kb + 4 G + v valid iff v <= lim
-    const int lim = k1 - 1 - kt - 16 * kb - 4 * G;
+    // keys >= cend masked: key 16 kb + 4 G + v valid iff v <= lim
+    const int lim = cend - 1 - kt - 16 * kb - 4 * G;
     float x[4];
 #pragma unroll
     for (int v = 0; v < 4; ++v) x[v] = v > lim ? -INFINITY : sc0[v] + sc1[v];
@@ -142,11 +215,9 @@ __device__ __forceinline__ void decode_segment(const uint16_t* __restrict__ q_la
       mt = max_xor32(max_xor16(mt));
       if (G == 0) mxbuf[(kb * 2 + qb) * 16 + n] = mt;
     }
-    __builtin_amdgcn_s_barrier();  // X: maxima posted; every wave is done with tile j - 1
-    // refill the buffer of tile j - 1
-    if (j + kDecodeBufs - 1 < ntile)
-      dma_tile32<R>(latb, k0 + kDecodeTileKeys * (j + kDecodeBufs - 1), k1,
-                    lds0 + ((j + kDecodeBufs - 1) % kDecodeBufs) * TILE, w);
+    __builtin_amdgcn_s_barrier();  // X: maxima posted; every wave is done with tile tau - 1
+    // refill the buffer of tile tau - 1
+    if (!ddone) copy_next();
     float alpha[2];
     bool grow_any = false;
 #pragma unroll
@@ -165,12 +236,9 @@ __device__ __forceinline__ void decode_segment(const uint16_t* __restrict__ q_la
       l_part = l_part * (qb ? alpha[1] : alpha[0]) + ((p0 + p1) + (p2 + p3));
       *(u32x2*)pw = u32x2{pack_bf16x2(p0, p1), pack_bf16x2(p2, p3)};
     }
-    // own part of tile j + 1 landed before the barrier that publishes P
-    if (j + 1 < ntile) {
-      const int last = j + kDecodeBufs - 1 < ntile - 1 ? j + kDecodeBufs - 1 : ntile - 1;
-      dma_wait_tiles<NI>(last - (j + 1));
-    }
-    __builtin_amdgcn_s_barrier();  // Y: P of tile j complete; tile j + 1 landed
+    // own part of tile tau + 1 landed before the barrier that publishes P
+    if (tau + 1 < issued) dma_wait_tiles<NI>(issued - tau - 2);
+    __builtin_amdgcn_s_barrier();  // Y: P of tile tau complete; tile tau + 1 landed
     if (__builtin_amdgcn_ballot_w64(grow_any)) {
       mfma_agpr_wait();
 #pragma unroll
@@ -184,9 +252,9 @@ __device__ __forceinline__ void decode_segment(const uint16_t* __restrict__ q_la
     }
     // ---- O^T += L^T P^T over this wave's columns.  Transpose read t of lane
     // (G, n): key 16 t + 4 G + n / 4, columns rw + 16 c + 4 (n % 4) .. + 3.
-    bf16x8 P[2];
+    bf16x8 Pq[2];
 #pragma unroll
-    for (int q = 0; q < 2; ++q) P[q] = lds_read16(pbuf + ((q * 4 + G) * 16 + n) * 16);
+    for (int q = 0; q < 2; ++q) Pq[q] = lds_read16(pbuf + ((q * 4 + G) * 16 + n) * 16);
 #pragma unroll
     for (int c = 0; c < NCW; ++c) {
       const int ch = (rw >> 3) + 2 * c + trh;
@@ -198,66 +266,20 @@ __device__ __forceinline__ void decode_segment(const uint16_t* __restrict__ q_la
                                                          __builtin_bit_cast(u32x2, a2[0])[1],
                                                          __builtin_bit_cast(u32x2, a2[1])[0],
                                                          __builtin_bit_cast(u32x2, a2[1])[1]});
-      mfma16x16x32_a(o[c][0], av, P[0]);
-      mfma16x16x32_a(o[c][1], av, P[1]);
+      mfma16x16x32_a(o[c][0], av, Pq[0]);
+      mfma16x16x32_a(o[c][1], av, Pq[1]);
     }
-  }
-
-  // ---- l of every head: partial sums of the two key halves through LDS
-  float lsum = l_part + __shfl_xor(l_part, 16);
-  lsum += __shfl_xor(lsum, 32);
-  __syncthreads();  // every wave is done with the P and maxima buffers
-  if (G == 0) mxbuf[(kb * 2 + qb) * 16 + n] = lsum;
-  __syncthreads();
-  mfma_agpr_wait();
-#pragma unroll
-  for (int q = 0; q < 2; ++q) {
-    const float lt = mxbuf[q * 16 + n] + mxbuf[(2 + q) * 16 + n];
-    const int hh = hg * 32 + 16 * q + n;
-    if (hh >= H) continue;
-    const float inv = 1.f / lt;
-    const size_t prow = (size_t)slot * H + hh;
-    uint16_t* po = part_o + prow * R + rw + 4 * G;
-#pragma unroll
-    for (int c = 0; c < NCW; ++c) {
-      mfma_agpr_tie(o[c][q]);
-      const u32x2 v = {pack_bf16x2(o[c][q][0] * inv, o[c][q][1] * inv),
-                       pack_bf16x2(o[c][q][2] * inv, o[c][q][3] * inv)};
-      *(u32x2*)(po + 16 * c) = v;
+    // ---- advance; at the end of a segment, its partial state and the next query
+    ck += kDecodeTileKeys;
+    if (ck >= cend) {
+      flush(cb);
+      ++cb;
+      if (!seg_more(cb)) break;
+      ck = 0;
+      cend = seg_end(cb);
+      load_q(cb);
+      reset();
     }
-    if (w == 0 && G == 0) {
-      part_ml[prow * 2] = m_run[q];
-      part_ml[prow * 2 + 1] = lt;
-    }
-  }
-}
-
-template <int R>
-__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
-void decode_split(const uint16_t* __restrict__ q_lat, const uint16_t* __restrict__ lat,
-                  const int32_t* __restrict__ S, uint16_t* __restrict__ part_o,
-                  float* __restrict__ part_ml, int B, int Tmax, int H, int P) {
-  __shared__ int first_seq;
-  const int g = blockIdx.x, hg = blockIdx.y;
-  const int N = S[B];
-  const int C = decode_chunk(N, P);
-  int x0 = (int)min((long long)g * C, (long long)N);
-  const int x1 = (int)min((long long)x0 + C, (long long)N);
-  if (x0 >= x1) return;  // whole block: chunk past the end
-  // sequence holding key x0 (S is nondecreasing with positive steps)
-  for (int i = threadIdx.x; i < B; i += 256)
-    if (S[i] <= x0 && x0 < S[i + 1]) first_seq = i;
-  __syncthreads();
-  int b = __builtin_amdgcn_readfirstlane(first_seq);
-  for (;;) {
-    const int sb = __builtin_amdgcn_readfirstlane(S[b]);
-    const int se = __builtin_amdgcn_readfirstlane(S[b + 1]);
-    const int xe = x1 < se ? x1 : se;
-    decode_segment<R>(q_lat, lat, part_o, part_ml, Tmax, H, hg, b, x0 - sb, xe - sb, g + b);
-    x0 = xe;
-    if (x0 >= x1) break;
-    ++b;
-    __syncthreads();  // the ring and exchange buffers are free for the next segment
   }
 }
 

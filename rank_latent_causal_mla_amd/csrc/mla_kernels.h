@@ -13,8 +13,8 @@ constexpr int decode_split_cap() { return 1024; }
 size_t decode_max_splits(int B);
 
 // LDS of the decode split kernel: a ring of four 32-key latent tiles, the
-// probabilities of one tile (2 KB) and 64 row maxima.
-constexpr size_t decode_lds_bytes(int R) { return (size_t)4 * 32 * R * 2 + 2048 + 256; }
+// probabilities of one tile (2 KB), 64 row maxima and 64 partial sums.
+constexpr size_t decode_lds_bytes(int R) { return (size_t)4 * 32 * R * 2 + 2048 + 512; }
 
 // LDS of the prefill flash kernel: a ring of four 32-key latent tiles, one
 // tile's probabilities for 128 rows (8 KB), 128 rescale factors and 4 flags.
