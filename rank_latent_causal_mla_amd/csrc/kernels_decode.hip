@@ -161,8 +161,7 @@ void decode_split(const uint16_t* __restrict__ q_lat, const uint16_t* __restrict
     float lsum = l_part + __shfl_xor(l_part, 16);
     lsum += __shfl_xor(lsum, 32);
     if (G == 0) lbuf[(kb * 2 + qb) * 16 + n] = lsum;
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    __builtin_amdgcn_s_barrier();
+    lds_publish_barrier();
     mfma_agpr_wait();
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
@@ -215,7 +214,7 @@ void decode_split(const uint16_t* __restrict__ q_lat, const uint16_t* __restrict
       mt = max_xor32(max_xor16(mt));
       if (G == 0) mxbuf[(kb * 2 + qb) * 16 + n] = mt;
     }
-    __builtin_amdgcn_s_barrier();  // X: maxima posted; every wave is done with tile tau - 1
+    lds_publish_barrier();  // X: maxima posted; every wave is done with tile tau - 1
     // refill the buffer of tile tau - 1
     if (!ddone) copy_next();
     float alpha[2];
@@ -238,7 +237,7 @@ void decode_split(const uint16_t* __restrict__ q_lat, const uint16_t* __restrict
     }
     // own part of tile tau + 1 landed before the barrier that publishes P
     if (tau + 1 < issued) dma_wait_tiles<NI>(issued - tau - 2);
-    __builtin_amdgcn_s_barrier();  // Y: P of tile tau complete; tile tau + 1 landed
+    lds_publish_barrier();  // Y: P of tile tau complete; tile tau + 1 landed
     if (__builtin_amdgcn_ballot_w64(grow_any)) {
       mfma_agpr_wait();
 #pragma unroll

@@ -450,7 +450,7 @@ void flash_latent_bf16(const uint16_t* __restrict__ q_lat, const uint16_t* __res
     // scores of tile j + 1 (after the last tile: a stale buffer, discarded)
     f32x4 s_next[2][2];
     F::scores(smem + ((j + 1) % kFlashBufs) * TILE, qf, s_next);
-    __builtin_amdgcn_s_barrier();  // P and rescale factors of tile j posted
+    lds_publish_barrier();  // P and rescale factors of tile j posted
     {
       const u32x4 f = *(const __attribute__((address_space(3))) u32x4*)(uintptr_t)fbuf;
       if ((f[0] | f[1] | f[2] | f[3]) != 0) {  // some row of the block has a new max

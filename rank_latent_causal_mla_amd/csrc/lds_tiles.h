@@ -36,6 +36,16 @@ __device__ __forceinline__ void dma_wait() {
   asm volatile("s_waitcnt vmcnt(%0)" : : "n"(n) : "memory");
 }
 
+// Barrier that publishes this wave's LDS writes to the other waves of the
+// block: the LDS serves the waves through several request queues, so a
+// write is only known to precede another wave's later read once the writer's
+// LDS counter has drained.  (A bare s_barrier orders instruction issue only;
+// the compiler adds no wait before it on this target.)
+__device__ __forceinline__ void lds_publish_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+}
+
 // Block-shared tile of 32 keys, row-major, 16-byte chunks XOR-swizzled by
 // tswz(key) inside every 16-chunk group:
 //   - score reads (16 lanes = 16 consecutive keys, one chunk each) hit 16
