@@ -316,40 +316,98 @@ struct Flash {
     }
   }
 
-  // Online-softmax update of the lane's two own rows for one tile (scores in
-  // log2 units: q_lat carries scale * log2 e).  With MASK, keys 16 kb + v
-  // (from k0 + 4 G) above lim[qb] are masked.  Returns whether any row's
-  // running max moved (then alpha != 1 for it).
+  // S^T of the next tile (into s) with the online-softmax update of the
+  // current one (scores sc) spread over its matrix ops: the update is cut
+  // into 40 pieces of a few vector instructions, and piece k is issued after
+  // matrix op k + kPieceLag, so it runs while the matrix unit is busy instead
+  // of between the two products.  Scores are in log2 units (q_lat carries
+  // scale * log2 e).  With MASK, keys 16 kb + v (from k0 + 4 G) above lim[qb]
+  // are masked.  Returns whether any row's running max moved (then
+  // alpha != 1 for it).
+  static constexpr int kPieceLag = 8;
   template <bool MASK>
-  static __device__ __forceinline__ bool softmax(const f32x4 (&s)[2][2], const int (&lim)[2], float (&m_run)[2],
-                                                 float (&l_run)[2], float (&alpha)[2], bf16x8 (&P)[2]) {
-    bool grow_any = false;
+  static __device__ __forceinline__ bool scores_softmax(const char* tile, const bf16x8 (*qf)[NKS], f32x4 (&s)[2][2],
+                                                        const f32x4 (&sc)[2][2], const int (&lim)[2], float (&m_run)[2],
+                                                        float (&l_run)[2], float (&alpha)[2], bf16x8 (&P)[2]) {
+    const int lane = threadIdx.x & 63;
+    const int G = lane >> 4, n = lane & 15;
+    const int f = tswz(n);
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      float x[8];
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int qb = 0; qb < 2; ++qb) s[kb][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    auto rd = [&](int i) {
+      const int kb = i & 1, ks = i >> 1;
+      const int c = 4 * ks + G;
+      return lds_read16(tile + (16 * kb + n) * (R * 2) + 16 * ((c & ~15) | ((c & 15) ^ f)));
+    };
+    float x[2][8], mm[2][4], mt[2], ps[2] = {0.f, 0.f}, msub[2];
+    bool grow[2];
+    uint32_t pk[2][4];
+    auto piece = [&](int k) {
+      if (k < 0) {
+      } else if (k < 8) {  // 0..7: masking and the lane's maximum of row block k / 4
+        const int qb = k >> 2, part = k & 3;
+        if (part == 0) {
 #pragma unroll
-        for (int v = 0; v < 4; ++v) x[4 * kb + v] = (MASK && 16 * kb + v > lim[qb]) ? -INFINITY : s[kb][qb][v];
-      float mt = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])), fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
-      mt = max_xor32(max_xor16(mt));
-      const bool grow = mt > m_run[qb] + kRescaleSlack;
-      alpha[qb] = grow ? fast_exp2(m_run[qb] - mt) : 1.f;
-      m_run[qb] = grow ? mt : m_run[qb];
-      grow_any |= grow;
-      const float msub = m_run[qb] == -INFINITY ? 0.f : m_run[qb];
-      float ps = 0.f;
-      uint32_t pk[4];
+          for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int u = 0; u < 8; u += 2) {
-        const float p0 = fast_exp2(x[u] - msub), p1 = fast_exp2(x[u + 1] - msub);
-        ps += p0 + p1;
-        pk[u >> 1] = pack_bf16x2(p0, p1);
+            for (int v = 0; v < 4; ++v)
+              x[qb][4 * kb + v] = (MASK && 16 * kb + v > lim[qb]) ? -INFINITY : sc[kb][qb][v];
+          mm[qb][0] = fmaxf(x[qb][0], x[qb][1]);
+          mm[qb][1] = fmaxf(x[qb][2], x[qb][3]);
+        } else if (part == 1) {
+          mm[qb][2] = fmaxf(x[qb][4], x[qb][5]);
+          mm[qb][3] = fmaxf(x[qb][6], x[qb][7]);
+        } else if (part == 2) {
+          mm[qb][0] = fmaxf(mm[qb][0], mm[qb][1]);
+          mm[qb][2] = fmaxf(mm[qb][2], mm[qb][3]);
+        } else {
+          mt[qb] = fmaxf(mm[qb][0], mm[qb][2]);
+        }
+      } else if (k < 12) {  // 8..11: maximum over the four lanes of a row
+        const int qb = k & 1;
+        mt[qb] = k < 10 ? max_xor16(mt[qb]) : max_xor32(mt[qb]);
+      } else if (k < 14) {  // 12, 13: rescale factor
+        const int qb = k & 1;
+        grow[qb] = mt[qb] > m_run[qb] + kRescaleSlack;
+        alpha[qb] = grow[qb] ? fast_exp2(m_run[qb] - mt[qb]) : 1.f;
+      } else if (k < 16) {  // 14, 15: running max
+        const int qb = k & 1;
+        m_run[qb] = grow[qb] ? mt[qb] : m_run[qb];
+        msub[qb] = m_run[qb] == -INFINITY ? 0.f : m_run[qb];
+      } else if (k < 32) {  // 16..31: probability u of row block qb, summed in pairs
+        const int qb = k & 1, u = (k - 16) >> 1;
+        x[qb][u] = fast_exp2(x[qb][u] - msub[qb]);
+        if (u & 1) ps[qb] += x[qb][u - 1] + x[qb][u];
+      } else if (k < 40) {  // 32..39: bf16 pairs, then the running sum and the P operand
+        const int qb = k & 1, u = (k - 32) >> 1;
+        pk[qb][u] = pack_bf16x2(x[qb][2 * u], x[qb][2 * u + 1]);
+        if (u == 3) {
+          l_run[qb] = l_run[qb] * alpha[qb] + ps[qb];
+          P[qb] = __builtin_bit_cast(bf16x8, u32x4{pk[qb][0], pk[qb][1], pk[qb][2], pk[qb][3]});
+        }
       }
-      l_run[qb] = l_run[qb] * alpha[qb] + ps;
-      P[qb] = __builtin_bit_cast(bf16x8, u32x4{pk[0], pk[1], pk[2], pk[3]});
+    };
+    constexpr int NR = 2 * NKS, DEPTH = 3;
+    bf16x8 ring[DEPTH];
+#pragma unroll
+    for (int i = 0; i < DEPTH; ++i) ring[i] = rd(i);
+#pragma unroll
+    for (int i = 0; i < NR; ++i) {
+      const bf16x8 av = ring[i % DEPTH];
+      if (i + DEPTH < NR) ring[i % DEPTH] = rd(i + DEPTH);
+      const int kb = i & 1, ks = i >> 1;
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        s[kb][qb] = mfma16x16x32(av, qf[qb][ks], s[kb][qb]);
+        piece(2 * i + qb - kPieceLag);
+        __builtin_amdgcn_sched_barrier(0);  // keep the piece after its matrix op
+      }
     }
-    return grow_any;
+#pragma unroll
+    for (int k = 2 * NR - kPieceLag; k < 40; ++k) piece(k);  // small R: fewer matrix ops than pieces
+    return grow[0] || grow[1];
   }
 };
 
@@ -438,8 +496,13 @@ void flash_latent_bf16(const uint16_t* __restrict__ q_lat, const uint16_t* __res
     for (int qb = 0; qb < 2; ++qb) lim[qb] = t_row[qb] - k0 - 4 * G;
     bf16x8 P[2];
     float alpha[2];
-    const bool grow = k0 + kTileKeys - 1 > t_first_w ? F::template softmax<true>(s_cur, lim, m_run, l_run, alpha, P)
-                                                     : F::template softmax<false>(s_cur, lim, m_run, l_run, alpha, P);
+    // scores of tile j + 1 (after the last tile: a stale buffer, discarded)
+    // with the softmax of tile j between their matrix ops
+    f32x4 s_next[2][2];
+    const char* ntile = smem + ((j + 1) % kFlashBufs) * TILE;
+    const bool grow = k0 + kTileKeys - 1 > t_first_w
+                          ? F::template scores_softmax<true>(ntile, qf, s_next, s_cur, lim, m_run, l_run, alpha, P)
+                          : F::template scores_softmax<false>(ntile, qf, s_next, s_cur, lim, m_run, l_run, alpha, P);
     // every wave passed the barrier that ended iteration j - 1: the exchange buffers are free
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
@@ -447,9 +510,6 @@ void flash_latent_bf16(const uint16_t* __restrict__ q_lat, const uint16_t* __res
       if (G == 0) abuf[(2 * w + qb) * 16 + n] = alpha[qb];
     }
     if (lane == 0) fbuf[w] = __builtin_amdgcn_ballot_w64(grow) != 0;
-    // scores of tile j + 1 (after the last tile: a stale buffer, discarded)
-    f32x4 s_next[2][2];
-    F::scores(smem + ((j + 1) % kFlashBufs) * TILE, qf, s_next);
     lds_publish_barrier();  // P and rescale factors of tile j posted
     {
       const u32x4 f = *(const __attribute__((address_space(3))) u32x4*)(uintptr_t)fbuf;

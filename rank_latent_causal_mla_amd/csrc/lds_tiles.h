@@ -46,13 +46,19 @@ __device__ __forceinline__ void lds_publish_barrier() {
   __builtin_amdgcn_s_barrier();
 }
 
-// Block-shared tile of 32 keys, row-major, 16-byte chunks XOR-swizzled by
-// tswz(key) inside every 16-chunk group:
-//   - score reads (16 lanes = 16 consecutive keys, one chunk each) hit 16
-//     distinct slots because tswz is a permutation of 0..15 on key % 16;
-//   - transpose reads (32 lanes = 8 consecutive keys x one chunk pair) hit 16
-//     distinct slots because tswz(key) >> 1 is a permutation of key % 8.
-__device__ __forceinline__ int tswz(int key) { return ((key & 7) << 1) | ((key >> 3) & 1); }
+// Block-shared tile of 32 keys, row-major (R * 2 bytes a row, a multiple of
+// 128), 16-byte chunks XOR-swizzled by tswz(key) inside every 16-chunk
+// group.  The LDS has 32 four-byte banks (128 bytes): a 16-byte read is
+// served 8 lanes at a time, an 8-byte transpose read 16 lanes at a time, and
+// lanes of one group conflict when their addresses share a bank.
+//   - score reads (lanes n = 0..15 of a 16-lane group: key row n, one chunk
+//     each): each 8-lane half needs 8 distinct chunk slots mod 8, so
+//     tswz(key) & 7 is a permutation of key & 7;
+//   - transpose reads (16 lanes: keys 4 g .. 4 g + 3, two adjacent chunks
+//     each, 32 bytes a key): the four keys need distinct 32-byte slots mod 4,
+//     so (tswz(key) >> 1) & 3 is a permutation of key & 3.
+// tswz(key + 16) = tswz(key), so rows n and 16 + n share the swizzle.
+__device__ __forceinline__ int tswz(int key) { return ((key & 3) << 1) | ((key >> 2) & 1) | (key & 8); }
 
 // Wave w's share of the LDS-DMA copy of one tile: instructions i = w, w + 4, ...
 // of the tile's 32 R * 2 / 1024, each 64 lanes x 16 bytes.  The swizzle is
