@@ -72,6 +72,15 @@ def prefill_flops(cfg) -> dict:
     return {"absorb": absorb, "attn": attn, "up": up, "down": down, "total": absorb + attn + up + down}
 
 
+def unabsorbed_flops(cfg) -> dict:
+    """FLOPs of one prefill call in unabsorbed form: k and v materialised
+    (2 B T r H d each), then causal attention at width d over t + 1 keys."""
+    B, T, H, d, r = cfg.B, cfg.T, cfg.H, cfg.d, cfg.r
+    kv = 2 * H * gemm_flops(B * T, r, d)
+    attn = 2 * B * H * d * T * (T + 1)          # scores + P v over s <= t
+    return {"materialise": kv, "attn": attn, "total": kv + attn}
+
+
 def decode_bytes(cfg, lens) -> dict:
     """Algorithmic HBM bytes of one decode call: the cached latents read once,
     both up-projection weights, q and out (bf16)."""
@@ -117,7 +126,7 @@ def kernel_times(fn, steps: int):
     return {k: {"avg_ms": tot / n, "launches": n} for k, (tot, n) in stats.items()}
 
 
-def bench_prefill(cfg, steps, warmup):
+def bench_prefill(cfg, steps, warmup, unabsorbed=False):
     import torch
     import synth
     import rank_latent_causal_mla_amd as mla
@@ -126,12 +135,12 @@ def bench_prefill(cfg, steps, warmup):
     dev = {k: to_device(v) for k, v in inp.items()}
     out = torch.empty_like(dev["q"])
     dt = mla.MLA_DTYPE_BF16 if cfg.dtype == "bf16" else mla.MLA_DTYPE_F32
-    ws = torch.empty(mla.mla_latent_attn_workspace_size(cfg.B, cfg.T, cfg.H, cfg.d, cfg.r, dt),
-                     dtype=torch.uint8, device="cuda")
+    size = mla.mla_latent_attn_unabsorbed_workspace_size if unabsorbed else mla.mla_latent_attn_workspace_size
+    fwd = mla.mla_latent_attn_fwd_unabsorbed if unabsorbed else mla.mla_latent_attn_fwd
+    ws = torch.empty(size(cfg.B, cfg.T, cfg.H, cfg.d, cfg.r, dt), dtype=torch.uint8, device="cuda")
 
     def step(_i):
-        mla.mla_latent_attn_fwd(dev["q"], dev["kv_latent"], dev["w_up_k"], dev["w_up_v"], out=out,
-                                scale=cfg.scale, workspace=ws)
+        fwd(dev["q"], dev["kv_latent"], dev["w_up_k"], dev["w_up_v"], out=out, scale=cfg.scale, workspace=ws)
 
     ms = time_steps(step, steps, warmup)
     kt = kernel_times(step, steps)
@@ -196,6 +205,7 @@ def main(argv=None):
     ap.add_argument("--decode-workload", default="bf16_decode")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-unabsorbed", action="store_true", help="skip the unabsorbed prefill timing")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (reference for HBM byte counters)")
     args = ap.parse_args(argv)
@@ -242,6 +252,23 @@ def main(argv=None):
         "roofline": roof,
         "kernels_ms": {k: round(v["avg_ms"], 4) for k, v in kt.items()},
     }
+    if not args.no_unabsorbed and cfg.dtype == "bf16" and \
+            mla.mla_latent_attn_unabsorbed_workspace_size(cfg.B, cfg.T, cfg.H, cfg.d, cfg.r, mla.MLA_DTYPE_BF16):
+        ums, ukt, _ = bench_prefill(cfg, args.steps, args.warmup, unabsorbed=True)
+        uw = unabsorbed_flops(cfg)
+        mha = ukt.get("flash_mha_bf16")
+        uroof = None
+        if mha:
+            ach = uw["attn"] / (mha["avg_ms"] * 1e-3) / 1e12
+            uroof = {"bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": measured_traffic("flash_mha_bf16"),
+                     "kernel": "flash_mha_bf16", "avg_ms": round(mha["avg_ms"], 4), "flops_per_launch": uw["attn"]}
+        line["unabsorbed"] = {
+            "what": "the same prefill with k and v materialised (mla_latent_attn_fwd_unabsorbed); value counts "
+                    "that form's own FLOPs",
+            "value": round(uw["total"] / (ums * 1e-3) / 1e12, 2), "unit": "TFLOP/s", "ms_per_step": round(ums, 4),
+            "flops_per_step": uw["total"], "step_time_vs_absorbed": round(ms / ums, 3), "roofline": uroof,
+            "kernels_ms": {k: round(v["avg_ms"], 4) for k, v in ukt.items()}}
     if not args.no_decode:
         dcfg = synth.CONFIGS[args.decode_workload]
         dms, dkt, lens = bench_decode(dcfg, max(args.steps, 10), args.warmup)

@@ -76,6 +76,24 @@ mla_status mla_latent_attn_fwd(const void* q, const void* kv_latent, const void*
                                int r, float scale, mla_dtype dt, void* workspace,
                                size_t workspace_bytes, void* stream);
 
+/* Bytes of workspace mla_latent_attn_fwd_unabsorbed needs for this shape
+ * (0 on bad sizes or a shape it does not cover). */
+size_t mla_latent_attn_unabsorbed_workspace_size(int B, int T, int H, int d, int r, mla_dtype dt);
+
+/* The same causal prefill as mla_latent_attn_fwd, same arguments and result
+ * up to rounding, computed in unabsorbed form: k and v of every head are
+ * materialised from kv_latent (page FW-GLM-5-1 l2_p1, operations list: the
+ * up-projections of the latent to keys and values), then causal attention
+ * runs over them with d-wide products.  At r > d this takes r/d times fewer
+ * matrix operations than the absorbed form, at the price of a workspace of
+ * 2*B*T*H*d elements (k and v).  Covers bf16 with d = 128 and
+ * r in {128, 256, 512}; other shapes and float32 return MLA_ERR_UNSUPPORTED.
+ * The logit scale is folded into the stored k (rounded once to bf16). */
+mla_status mla_latent_attn_fwd_unabsorbed(const void* q, const void* kv_latent, const void* w_up_k,
+                                          const void* w_up_v, void* out, int B, int T, int H, int d,
+                                          int r, float scale, mla_dtype dt, void* workspace,
+                                          size_t workspace_bytes, void* stream);
+
 /* Bytes of workspace mla_decode_fwd needs for this shape (0 on bad sizes). */
 size_t mla_decode_workspace_size(int B, int Tmax, int H, int d, int r, mla_dtype dt);
 

@@ -19,6 +19,7 @@ MLA_OK, MLA_ERR_INVALID_ARGUMENT, MLA_ERR_UNSUPPORTED, MLA_ERR_WORKSPACE, MLA_ER
 MLA_DTYPE_F32, MLA_DTYPE_BF16 = 0, 1
 
 EXPORTED = ("mla_down_proj", "mla_latent_attn_workspace_size", "mla_latent_attn_fwd",
+            "mla_latent_attn_unabsorbed_workspace_size", "mla_latent_attn_fwd_unabsorbed",
             "mla_decode_workspace_size", "mla_decode_fwd", "mla_profile_enable", "mla_profile_collect",
             "mla_status_string", "mla_last_error")
 
@@ -46,6 +47,10 @@ def load():
     lib.mla_latent_attn_workspace_size.argtypes = [i32] * 6
     lib.mla_latent_attn_fwd.restype = i32
     lib.mla_latent_attn_fwd.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, i32, vp, sz, vp]
+    lib.mla_latent_attn_unabsorbed_workspace_size.restype = sz
+    lib.mla_latent_attn_unabsorbed_workspace_size.argtypes = [i32] * 6
+    lib.mla_latent_attn_fwd_unabsorbed.restype = i32
+    lib.mla_latent_attn_fwd_unabsorbed.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, i32, vp, sz, vp]
     lib.mla_decode_workspace_size.restype = sz
     lib.mla_decode_workspace_size.argtypes = [i32] * 6
     lib.mla_decode_fwd.restype = i32
@@ -86,6 +91,10 @@ def mla_latent_attn_workspace_size(B, T, H, d, r, dt):
     return int(load().mla_latent_attn_workspace_size(B, T, H, d, r, dt))
 
 
+def mla_latent_attn_unabsorbed_workspace_size(B, T, H, d, r, dt):
+    return int(load().mla_latent_attn_unabsorbed_workspace_size(B, T, H, d, r, dt))
+
+
 def mla_decode_workspace_size(B, Tmax, H, d, r, dt):
     return int(load().mla_decode_workspace_size(B, Tmax, H, d, r, dt))
 
@@ -93,6 +102,12 @@ def mla_decode_workspace_size(B, Tmax, H, d, r, dt):
 def mla_latent_attn_fwd_raw(q, kv_latent, w_up_k, w_up_v, out, B, T, H, d, r, scale, dt, ws, ws_bytes, stream=0):
     return load().mla_latent_attn_fwd(q, kv_latent, w_up_k, w_up_v, out, B, T, H, d, r, scale, dt, ws,
                                       ws_bytes, stream)
+
+
+def mla_latent_attn_fwd_unabsorbed_raw(q, kv_latent, w_up_k, w_up_v, out, B, T, H, d, r, scale, dt, ws, ws_bytes,
+                                       stream=0):
+    return load().mla_latent_attn_fwd_unabsorbed(q, kv_latent, w_up_k, w_up_v, out, B, T, H, d, r, scale, dt, ws,
+                                                 ws_bytes, stream)
 
 
 def mla_decode_fwd_raw(q, kv_latent, seq_lens, w_up_k, w_up_v, out, B, Tmax, H, d, r, scale, dt, ws,
@@ -173,6 +188,29 @@ def mla_latent_attn_fwd(q, kv_latent, w_up_k, w_up_v, out=None, scale=None, work
     _check(mla_latent_attn_fwd_raw(q.data_ptr(), kv_latent.data_ptr(), w_up_k.data_ptr(), w_up_v.data_ptr(),
                                    out.data_ptr(), B, T, H, d, r, float(scale), dt, workspace.data_ptr(),
                                    workspace.numel() * workspace.element_size(), _stream(stream)))
+    return out
+
+
+def mla_latent_attn_fwd_unabsorbed(q, kv_latent, w_up_k, w_up_v, out=None, scale=None, workspace=None,
+                                   stream=None):
+    """The same prefill in unabsorbed form (k, v materialised; bf16, d = 128, r in {128, 256, 512})."""
+    import torch
+    _dev(q, kv_latent, w_up_k, w_up_v)
+    B, T, H, d = q.shape
+    r = kv_latent.shape[-1]
+    dt = _dt(q)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    nbytes = mla_latent_attn_unabsorbed_workspace_size(B, T, H, d, r, dt)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    _dev(out, workspace)
+    _check(mla_latent_attn_fwd_unabsorbed_raw(q.data_ptr(), kv_latent.data_ptr(), w_up_k.data_ptr(),
+                                              w_up_v.data_ptr(), out.data_ptr(), B, T, H, d, r, float(scale), dt,
+                                              workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                                              _stream(stream)))
     return out
 
 

@@ -7,7 +7,8 @@ import subprocess
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 SO = os.path.join(HERE, "libmla.so")
-SOURCES = ["mla_api.hip", "kernels_mfma.hip", "kernels_decode.hip", "kernels_simt.hip", "profile.hip"]
+SOURCES = ["mla_api.hip", "kernels_mfma.hip", "kernels_unabsorbed.hip", "kernels_decode.hip", "kernels_simt.hip",
+           "profile.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 # -packed-fp32-ops: no v_pk_{add,mul,fma}_f32 in any kernel.

@@ -167,8 +167,10 @@ hipError_t transpose_wv_launch(const uint16_t* wv, uint16_t* wvT, int R, int H, 
 }
 
 // ---------------------------------------------------------------------------
-// Up-projection: out[n, h, e] = sum_rho o_lat[n*H + h, rho] * W_uv[rho, h, e],
-// computed as out^T = W_uv^T o_lat^T.  Block: head h, output columns
+// Up-projection: out[n, h, e] = oscale * sum_rho src[row, rho] * W[rho, h, e]
+// with row = n*H + h (per-head rows: o_lat) or, with SHARED, row = n (one
+// row for all heads: the latent, when k or v are materialised), computed as
+// out^T = W^T src^T from W^T [H][d][R].  Block: head h, output columns
 // e = 128 blockIdx.z + 32 w .. (wave w holds that slice of W_uv^T in
 // registers), and row blocks kUpRowBlocks * blockIdx.x .. of 32 rows.  The
 // o_lat rows of a row block are copied once per block into LDS by LDS-DMA
@@ -178,10 +180,10 @@ constexpr int kUpRowBlocks = 8;
 template <int R>
 constexpr size_t up_lds_bytes() { return (size_t)2 * 32 * R * 2; }
 
-template <int R>
+template <int R, bool SHARED>
 __global__ __launch_bounds__(256, 2) void up_bf16(const uint16_t* __restrict__ o_lat,
                                                   const uint16_t* __restrict__ wvT,
-                                                  uint16_t* __restrict__ out, int N, int H, int d) {
+                                                  uint16_t* __restrict__ out, int N, int H, int d, float oscale) {
   constexpr int NKS = R / 16;           // contraction steps
   constexpr int TB = 32 * R * 2;        // one row block in LDS
   constexpr int NC = R / 8;             // 16-byte chunks per row
@@ -218,8 +220,11 @@ __global__ __launch_bounds__(256, 2) void up_bf16(const uint16_t* __restrict__ o
       const int n = min(32 * (nb0 + k) + s, N - 1);
       const int n0 = __builtin_amdgcn_readfirstlane(min(32 * (nb0 + k) + ins * RPI, N - 1));
       const int c = (p & ~15) | ((p & 15) ^ (s & 15));
-      dma16(o_lat + ((size_t)n0 * H + h) * R, (uint32_t)(((size_t)(n - n0) * H) * R * 2 + 16 * c),
-            lds0 + (k & 1) * TB + ins * 1024);
+      if (SHARED)
+        dma16(o_lat + (size_t)n0 * R, (uint32_t)((n - n0) * R * 2 + 16 * c), lds0 + (k & 1) * TB + ins * 1024);
+      else
+        dma16(o_lat + ((size_t)n0 * H + h) * R, (uint32_t)(((size_t)(n - n0) * H) * R * 2 + 16 * c),
+              lds0 + (k & 1) * TB + ins * 1024);
     }
   };
   copy(0);
@@ -248,8 +253,9 @@ __global__ __launch_bounds__(256, 2) void up_bf16(const uint16_t* __restrict__ o
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int e = 32 * i + 8 * j + 4 * g;
-          u32x2 v = {pack_bf16x2(acc0[4 * j] + acc1[4 * j], acc0[4 * j + 1] + acc1[4 * j + 1]),
-                     pack_bf16x2(acc0[4 * j + 2] + acc1[4 * j + 2], acc0[4 * j + 3] + acc1[4 * j + 3])};
+          u32x2 v = {pack_bf16x2((acc0[4 * j] + acc1[4 * j]) * oscale, (acc0[4 * j + 1] + acc1[4 * j + 1]) * oscale),
+                     pack_bf16x2((acc0[4 * j + 2] + acc1[4 * j + 2]) * oscale,
+                                 (acc0[4 * j + 3] + acc1[4 * j + 3]) * oscale)};
           *(u32x2*)(dst + e) = v;
         }
       }
@@ -594,7 +600,7 @@ static hipError_t run_prefill(const uint16_t* q, const uint16_t* lat, const uint
     hipError_t e = hipFuncSetAttribute((const void*)flash_latent_bf16<R>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)flash_lds_bytes(R));
     if (e == hipSuccess)
-      e = hipFuncSetAttribute((const void*)up_bf16<R>, hipFuncAttributeMaxDynamicSharedMemorySize,
+      e = hipFuncSetAttribute((const void*)up_bf16<R, false>, hipFuncAttributeMaxDynamicSharedMemorySize,
                               (int)up_lds_bytes<R>());
     if (e != hipSuccess) return e;
     attr_set = true;
@@ -615,8 +621,8 @@ static hipError_t run_prefill(const uint16_t* q, const uint16_t* lat, const uint
   }
   {
     ProfScope ps("up_bf16", st);
-    hipLaunchKernelGGL(up_bf16<R>, dim3((N + 32 * kUpRowBlocks - 1) / (32 * kUpRowBlocks), H, (d + 127) / 128),
-                       dim3(256), up_lds_bytes<R>(), st, o_lat, wvT, out, N, H, d);
+    hipLaunchKernelGGL((up_bf16<R, false>), dim3((N + 32 * kUpRowBlocks - 1) / (32 * kUpRowBlocks), H, (d + 127) / 128),
+                       dim3(256), up_lds_bytes<R>(), st, o_lat, wvT, out, N, H, d, 1.0f);
   }
   return hipGetLastError();
 }
@@ -636,6 +642,46 @@ hipError_t prefill_mfma(const void* q, const void* lat, const void* wk, const vo
     case 512: return run_prefill<512>(ARGS);
   }
 #undef ARGS
+  return hipErrorInvalidValue;
+}
+
+// k and v of every head from the shared latent (the unabsorbed form):
+// k[n, h, :] = kscale * latent[n, :] W_uk[:, h, :], v[n, h, :] = latent[n, :] W_uv[:, h, :],
+// both [N][H][d] bf16; wkT, wvT: [H][d][R] transposes in the workspace.
+template <int R>
+static hipError_t run_materialise(const uint16_t* lat, const uint16_t* wk, const uint16_t* wv, uint16_t* k,
+                                  uint16_t* v, uint16_t* wkT, uint16_t* wvT, int N, int H, int d, float kscale,
+                                  hipStream_t st) {
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute((const void*)up_bf16<R, true>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       (int)up_lds_bytes<R>());
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  hipError_t e;
+  {
+    ProfScope ps("transpose_wv", st);
+    e = transpose_wv_launch(wk, wkT, R, H, d, st);
+    if (e == hipSuccess) e = transpose_wv_launch(wv, wvT, R, H, d, st);
+    if (e != hipSuccess) return e;
+  }
+  const dim3 grid((N + 32 * kUpRowBlocks - 1) / (32 * kUpRowBlocks), H, (d + 127) / 128);
+  {
+    ProfScope ps("materialise_kv", st);
+    hipLaunchKernelGGL((up_bf16<R, true>), grid, dim3(256), up_lds_bytes<R>(), st, lat, wkT, k, N, H, d, kscale);
+    hipLaunchKernelGGL((up_bf16<R, true>), grid, dim3(256), up_lds_bytes<R>(), st, lat, wvT, v, N, H, d, 1.0f);
+  }
+  return hipGetLastError();
+}
+
+hipError_t materialise_kv(const uint16_t* lat, const uint16_t* wk, const uint16_t* wv, uint16_t* k, uint16_t* v,
+                          uint16_t* wkT, uint16_t* wvT, int N, int H, int d, int r, float kscale, hipStream_t st) {
+  switch (r) {
+    case 128: return run_materialise<128>(lat, wk, wv, k, v, wkT, wvT, N, H, d, kscale, st);
+    case 256: return run_materialise<256>(lat, wk, wv, k, v, wkT, wvT, N, H, d, kscale, st);
+    case 512: return run_materialise<512>(lat, wk, wv, k, v, wkT, wvT, N, H, d, kscale, st);
+  }
   return hipErrorInvalidValue;
 }
 

@@ -137,6 +137,41 @@ mla_status mla_latent_attn_fwd(const void* q, const void* kv_latent, const void*
                   "prefill launch");
 }
 
+size_t mla_latent_attn_unabsorbed_workspace_size(int B, int T, int H, int d, int r, mla_dtype dt) {
+  if (B < 1 || T < 1 || H < 1 || d < 1 || r < 1) return 0;
+  if (dt != MLA_DTYPE_BF16 || !mla::unabsorbed_supported(d, r)) return 0;
+  return mla::prefill_unabsorbed_workspace(B, T, H, d, r);
+}
+
+mla_status mla_latent_attn_fwd_unabsorbed(const void* q, const void* kv_latent, const void* w_up_k,
+                                          const void* w_up_v, void* out, int B, int T, int H, int d, int r,
+                                          float scale, mla_dtype dt, void* workspace, size_t workspace_bytes,
+                                          void* stream) {
+  if (!q || !kv_latent || !w_up_k || !w_up_v || !out || !workspace)
+    return fail(MLA_ERR_INVALID_ARGUMENT, "null pointer");
+  mla_status s = check_dims(B, T, H, d, r, dt, "T");
+  if (s != MLA_OK) return s;
+  if (!std::isfinite(scale)) return fail(MLA_ERR_INVALID_ARGUMENT, "scale must be finite");
+  if (!aligned16(q) || !aligned16(kv_latent) || !aligned16(w_up_k) || !aligned16(w_up_v) ||
+      !aligned16(out) || !aligned16(workspace))
+    return fail(MLA_ERR_INVALID_ARGUMENT, "pointers must be 16-byte aligned");
+  if (dt != MLA_DTYPE_BF16 || !mla::unabsorbed_supported(d, r))
+    return fail(MLA_ERR_UNSUPPORTED, "unabsorbed prefill covers bf16 with d = 128, r in {128, 256, 512} "
+                "(got %s, d=%d, r=%d)", dt == MLA_DTYPE_BF16 ? "bf16" : "float32", d, r);
+  const size_t need = mla_latent_attn_unabsorbed_workspace_size(B, T, H, d, r, dt);
+  if (workspace_bytes < need)
+    return fail(MLA_ERR_WORKSPACE, "workspace %zu bytes < %zu required", workspace_bytes, need);
+  size_t limit = 0;
+  s = device_lds_limit(&limit);
+  if (s != MLA_OK) return s;
+  if (mla::unabsorbed_lds_bytes(d) > limit)
+    return fail(MLA_ERR_UNSUPPORTED, "unabsorbed prefill needs %zu bytes of LDS per block, device allows %zu",
+                mla::unabsorbed_lds_bytes(d), limit);
+  return launched(mla::prefill_unabsorbed(q, kv_latent, w_up_k, w_up_v, out, B, T, H, d, r,
+                                          (float)(scale * kLog2e), workspace, (hipStream_t)stream),
+                  "unabsorbed prefill launch");
+}
+
 size_t mla_decode_workspace_size(int B, int Tmax, int H, int d, int r, mla_dtype dt) {
   if (B < 1 || Tmax < 1 || H < 1 || d < 1 || r < 1) return 0;
   if (dt != MLA_DTYPE_F32 && dt != MLA_DTYPE_BF16) return 0;

@@ -124,12 +124,6 @@ __device__ __forceinline__ void wait_vmem_outstanding() {
   __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-// XOR swizzle of 16-byte chunks inside a 16-chunk group of a row-major LDS
-// tile row s: f is a bijection on 0..15, so one chunk read from 16
-// consecutive rows hits 16 distinct 16-byte bank groups, and 4 consecutive
-// rows map an aligned chunk pair to 4 distinct pairs (transpose reads).
-__device__ __forceinline__ int swz(int s) { return ((s & 3) << 2) | ((s >> 2) & 3); }
-
 // Slack (log2 units) the online-softmax reference max may lag the running
 // max before the accumulators are rescaled; probabilities then stay <= 2^8.
 // The normalised result does not depend on it.

@@ -35,6 +35,17 @@ hipError_t absorb_mfma(const uint16_t* q, const uint16_t* wk, uint16_t* q_lat, i
 // W_uv [R, H, d] -> W_uv^T [H, d, R].
 hipError_t transpose_wv_launch(const uint16_t* wv, uint16_t* wvT, int R, int H, int d, hipStream_t st);
 
+// ---- unabsorbed prefill (bf16, d = 128, r in {128, 256, 512}): k and v
+// materialised in the workspace, then causal flash attention over them
+bool unabsorbed_supported(int d, int r);
+size_t unabsorbed_lds_bytes(int d);
+size_t prefill_unabsorbed_workspace(int B, int T, int H, int d, int r);
+hipError_t prefill_unabsorbed(const void* q, const void* lat, const void* wk, const void* wv, void* out, int B,
+                              int T, int H, int d, int r, float sl2, void* ws, hipStream_t st);
+// k [N][H][d] = kscale * latent W_uk, v [N][H][d] = latent W_uv (wkT, wvT: [H][d][r] scratch)
+hipError_t materialise_kv(const uint16_t* lat, const uint16_t* wk, const uint16_t* wv, uint16_t* k, uint16_t* v,
+                          uint16_t* wkT, uint16_t* wvT, int N, int H, int d, int r, float kscale, hipStream_t st);
+
 // ---- SIMT path: float32 (or bf16 storage) with float32 arithmetic, any r <= 1024, d <= 256
 // dt_bf16: inputs and outputs stored as bf16 (else float32).
 hipError_t prefill_simt(bool dt_bf16, const void* q, const void* lat, const void* wk,

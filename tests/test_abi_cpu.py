@@ -71,6 +71,39 @@ def test_argument_errors(fn, kw, status):
     assert mla.last_error() != ""
 
 
+def unabs(**kw):
+    a = dict(q=P, kv=P, wk=P, wv=P, out=P, B=2, T=64, H=4, d=128, r=512, scale=0.09, dt=BF16, ws=P, wsb=1 << 40)
+    a.update(kw)
+    return mla.mla_latent_attn_fwd_unabsorbed_raw(a["q"], a["kv"], a["wk"], a["wv"], a["out"], a["B"], a["T"],
+                                                  a["H"], a["d"], a["r"], a["scale"], a["dt"], a["ws"], a["wsb"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    ({"q": 0}, mla.MLA_ERR_INVALID_ARGUMENT),
+    ({"ws": 0}, mla.MLA_ERR_INVALID_ARGUMENT),
+    ({"T": 0}, mla.MLA_ERR_INVALID_ARGUMENT),
+    ({"dt": 7}, mla.MLA_ERR_INVALID_ARGUMENT),
+    ({"scale": float("inf")}, mla.MLA_ERR_INVALID_ARGUMENT),
+    ({"out": P + 8}, mla.MLA_ERR_INVALID_ARGUMENT),
+    ({"dt": F32}, mla.MLA_ERR_UNSUPPORTED),
+    ({"d": 64}, mla.MLA_ERR_UNSUPPORTED),
+    ({"r": 48}, mla.MLA_ERR_UNSUPPORTED),
+    ({"r": 2048}, mla.MLA_ERR_UNSUPPORTED),
+    ({"wsb": 1 << 20}, mla.MLA_ERR_WORKSPACE),
+])
+def test_unabsorbed_argument_errors(kw, status):
+    assert unabs(**kw) == status
+    assert mla.last_error() != ""
+
+
+def test_unabsorbed_workspace_size():
+    # k and v [B*T][H][d] plus W_uk^T and W_uv^T [H][d][r], bf16
+    assert mla.mla_latent_attn_unabsorbed_workspace_size(2, 64, 4, 128, 512, BF16) == \
+        (2 * 2 * 64 * 4 * 128 + 2 * 4 * 128 * 512) * 2
+    assert mla.mla_latent_attn_unabsorbed_workspace_size(2, 64, 4, 128, 512, F32) == 0
+    assert mla.mla_latent_attn_unabsorbed_workspace_size(2, 64, 4, 64, 512, BF16) == 0
+
+
 def test_decode_null_lengths():
     assert dec(lens=0) == mla.MLA_ERR_INVALID_ARGUMENT
     assert dec(lens=P + 2) == mla.MLA_ERR_INVALID_ARGUMENT

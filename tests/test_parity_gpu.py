@@ -28,14 +28,15 @@ def cfg_like(name, **kw):
     return dataclasses.replace(synth.CONFIGS[name], **kw)
 
 
-def run_prefill(cfg, inp):
+def run_prefill(cfg, inp, fwd=None):
     import torch
+    fwd = fwd or mla.mla_latent_attn_fwd
     dev = {k: to_device(v) for k, v in inp.items() if k != "seq_lens"}
     if cfg.D:
         lat = mla.mla_down_proj(dev["hidden"], dev["w_down"])
     else:
         lat = dev["kv_latent"]
-    out = mla.mla_latent_attn_fwd(dev["q"], lat, dev["w_up_k"], dev["w_up_v"], scale=cfg.scale)
+    out = fwd(dev["q"], lat, dev["w_up_k"], dev["w_up_v"], scale=cfg.scale)
     torch.cuda.synchronize()
     return out, lat
 
@@ -84,16 +85,16 @@ def test_full_path_config():
 
 
 # ---------------------------------------------------------------- prefill at full size, sampled rows
-def sampled_prefill(cfg, heads, rows_per_head, seed=1):
+def sampled_prefill(cfg, heads, rows_per_head, seed=1, fwd=None):
     import torch
     inp = synth.make_inputs(cfg)
-    print(f"full-size prefill {cfg.name}", flush=True)
-    out, _ = run_prefill(cfg, inp)
+    print(f"full-size prefill {cfg.name} {'' if fwd is None else fwd.__name__}", flush=True)
+    out, _ = run_prefill(cfg, inp, fwd)
     out = out.float()
     assert torch.isfinite(out).all().item()
     rng = np.random.default_rng(seed)
     T = cfg.T
-    fixed = [0, 1, 31, 32, 33, 127, 128, T // 2, T - 2, T - 1]
+    fixed = [0, 1, 31, 32, 33, 127, 128, 255, 256, T // 2, T - 2, T - 1]
     rb, rh, rt = [], [], []
     for (b, h) in heads:
         ts = sorted(set(fixed + list(rng.integers(0, T, rows_per_head))))
@@ -116,6 +117,49 @@ def test_bf16_prefill_full_size_sampled():
 
 def test_bf16_long_prefill_full_size_sampled():
     sampled_prefill(synth.CONFIGS["bf16_long_prefill"], heads=[(0, 0), (1, 63)], rows_per_head=12)
+
+
+# ---------------------------------------------------------------- unabsorbed prefill (k, v materialised)
+UNABSORBED_SMALL = [
+    dict(B=2, T=300, H=3),            # two 256-row blocks, ragged tail, ring of six tiles wrapped
+    dict(B=1, T=520, H=1),            # 17 tiles: the ring wraps twice; partial last row block
+    dict(B=3, T=1, H=2),              # single key
+    dict(B=1, T=33, H=4, r=256),      # r = 256
+    dict(B=2, T=65, H=2, r=128),      # r = 128
+    dict(B=1, T=64, H=2),             # a whole number of tiles, fewer than the copy distance
+]
+
+
+@pytest.mark.parametrize("kw", UNABSORBED_SMALL, ids=[f"unabsorbed-{i}" for i in range(len(UNABSORBED_SMALL))])
+def test_unabsorbed_prefill_matches_oracle(kw):
+    cfg = cfg_like("bf16_prefill", **kw)
+    inp = synth.make_inputs(cfg)
+    print(f"unabsorbed prefill parity {cfg}", flush=True)
+    out, _ = run_prefill(cfg, inp, mla.mla_latent_attn_fwd_unabsorbed)
+    ref = oracle_prefill(cfg, inp)
+    err = compare(to_f64(out), ref, cfg.dtype, cfg.name)
+    print(f"max abs err {err:.3e}")
+    tight(to_f64(out), ref)
+
+
+def test_unabsorbed_bf16_prefill_full_size_sampled():
+    sampled_prefill(synth.CONFIGS["bf16_prefill"], heads=[(0, 0), (3, 7), (7, 15)], rows_per_head=24,
+                    fwd=mla.mla_latent_attn_fwd_unabsorbed)
+
+
+def test_unabsorbed_bf16_long_prefill_full_size_sampled():
+    sampled_prefill(synth.CONFIGS["bf16_long_prefill"], heads=[(0, 0), (1, 63)], rows_per_head=12,
+                    fwd=mla.mla_latent_attn_fwd_unabsorbed)
+
+
+def test_unabsorbed_rejects_float32():
+    import torch
+    cfg = synth.CONFIGS["fp32_small"]
+    inp = synth.make_inputs(cfg)
+    dev = {k: to_device(v) for k, v in inp.items() if k != "seq_lens"}
+    with pytest.raises(mla.MLAError):
+        mla.mla_latent_attn_fwd_unabsorbed(dev["q"], dev["kv_latent"], dev["w_up_k"], dev["w_up_v"])
+    torch.cuda.synchronize()
 
 
 # ---------------------------------------------------------------- decode
