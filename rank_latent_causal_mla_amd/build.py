@@ -12,12 +12,15 @@ SOURCES = ["mla_api.hip", "kernels_mfma.hip", "kernels_unabsorbed.hip", "kernels
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 # -packed-fp32-ops: no v_pk_{add,mul,fma}_f32 in any kernel.
+# -fno-honor-nans: max/min need not quiet signalling NaNs, so fmaxf is one
+# v_max_f32 instead of two canonicalising ops plus the max (the softmax
+# compares against +-infinity only; a NaN input gives a non-finite output).
 # -amdgpu-mfma-vgpr-form: matrix instructions written with the builtins keep
 # their accumulators in VGPRs; the flash kernels pin their large output
 # accumulators to AGPRs explicitly (inline asm), so the two never compete.
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-shared", "-fPIC",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-         "-mllvm", "-amdgpu-mfma-vgpr-form=true",
+         "-mllvm", "-amdgpu-mfma-vgpr-form=true", "-fno-honor-nans",
          "-I", os.path.join(ROOT, "include")]
 
 

@@ -186,11 +186,13 @@ void flash_mha_bf16(const uint16_t* __restrict__ q, const uint16_t* __restrict__
 #pragma unroll
   for (int qb = 0; qb < NQB; ++qb) P_prev[qb] = bf16x8{};
 
-  for (int j = 0; j < ntiles; ++j) {
+  // Iteration j; with MASK, keys above a row's position are masked (only
+  // tiles that reach past the wave's first row need it).
+  auto body = [&](int j, auto maskc) __attribute__((always_inline)) {
+    constexpr bool mask = decltype(maskc)::value;
     const int k0 = kTileKeys * j;
     const char* ktile = smem + ((j + 1) % kMhaBufs) * TILE;                   // scores of tile j + 1
     const char* vtile = smem + ((j > 0 ? j - 1 : 0) % kMhaBufs) * TILE + KT;  // P*V of tile j - 1
-    const bool mask = k0 + kTileKeys - 1 > tw0;
     int lim[NQB];
 #pragma unroll
     for (int qb = 0; qb < NQB; ++qb) lim[qb] = t_row[qb] - k0 - 4 * G;
@@ -308,7 +310,10 @@ void flash_mha_bf16(const uint16_t* __restrict__ q, const uint16_t* __restrict__
     // own part of tile j + 2 landed before the barrier that ends the iteration
     if (j + 2 < ntiles) wait_tile(j + 2, issued);
     __builtin_amdgcn_s_barrier();
-  }
+  };
+  const int jm = tw0 / kTileKeys < ntiles ? tw0 / kTileKeys : ntiles;  // tiles below every row of the wave
+  for (int j = 0; j < jm; ++j) body(j, std::false_type{});
+  for (int j = jm; j < ntiles; ++j) body(j, std::true_type{});
 
   // P*V of the last tile
   {
