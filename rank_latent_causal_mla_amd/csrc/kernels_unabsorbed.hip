@@ -232,7 +232,9 @@ void flash_mha_bf16(const uint16_t* __restrict__ q, const uint16_t* __restrict__
       } else if (kp < 32) {  // running max
         const int qb = kp & 3;
         m_run[qb] = grow[qb] ? mt[qb] : m_run[qb];
-        msub[qb] = m_run[qb] == -INFINITY ? 0.f : m_run[qb];
+        // finite from tile 0 on: key 0 is unmasked for every row, so the
+        // first tile always moves the running max off -infinity
+        msub[qb] = m_run[qb];
         ps[qb] = 0.f;
       } else if (kp < 64) {  // probability u of row block qb, summed in pairs
         const int qb = kp & 3, u = (kp - 32) >> 2;
