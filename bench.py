@@ -147,6 +147,30 @@ def bench_prefill(cfg, steps, warmup, unabsorbed=False):
     return ms, kt, inp
 
 
+def bench_decode_varlen(cfg, steps, warmup, copies=3):
+    """The same decode over packed caches [sum L, r] with cu_seqlens (rotated copies as above)."""
+    import torch
+    import synth
+    import rank_latent_causal_mla_amd as mla
+    from tests.helpers import to_device
+    inp = synth.make_inputs(cfg)
+    lens = inp["seq_lens"]
+    dev = {k: to_device(v) for k, v in inp.items() if k not in ("seq_lens", "kv_latent")}
+    packed = np.concatenate([inp["kv_latent"][b, :int(L)] for b, L in enumerate(lens)], axis=0)
+    cu = torch.from_numpy(np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)).cuda()
+    caches = [to_device(packed)]
+    caches += [caches[0].clone() for _ in range(copies - 1)]
+    out = torch.empty_like(dev["q"])
+    ws = torch.empty(mla.mla_decode_varlen_workspace_size(cfg.B, packed.shape[0], cfg.H, cfg.d, cfg.r,
+                                                          mla.MLA_DTYPE_BF16), dtype=torch.uint8, device="cuda")
+
+    def step(i):
+        mla.mla_decode_varlen_fwd(dev["q"], caches[i % copies], cu, dev["w_up_k"], dev["w_up_v"], out=out,
+                                  scale=cfg.scale, workspace=ws)
+
+    return time_steps(step, steps, warmup)
+
+
 def bench_decode(cfg, steps, warmup, copies=3):
     """Decode with `copies` independent caches used in turn, so the 256 MB
     last-level cache cannot hold the ~300 MB working set between steps."""
@@ -285,6 +309,11 @@ def main(argv=None):
                           "unit": "GB/s", "ms_per_step": round(dms, 4), "bytes_per_step": db["total"],
                           "sum_seq_lens": int(np.sum(lens)), "roofline": droof,
                           "kernels_ms": {k: round(v["avg_ms"], 4) for k, v in dkt.items()}}
+        if dcfg.dtype == "bf16":
+            vms = bench_decode_varlen(dcfg, max(args.steps, 10), args.warmup)
+            line["decode"]["varlen"] = {"what": "the same decode over a packed cache (mla_decode_varlen_fwd)",
+                                        "value": round(db["total"] / (vms * 1e-3) / 1e9, 1), "unit": "GB/s",
+                                        "ms_per_step": round(vms, 4)}
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(cfg, inp)
     print(json.dumps(line), flush=True)

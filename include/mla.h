@@ -111,6 +111,38 @@ mla_status mla_decode_fwd(const void* q, const void* kv_latent, const int32_t* s
                           int H, int d, int r, float scale, mla_dtype dt, void* workspace,
                           size_t workspace_bytes, void* stream);
 
+/* Bytes of workspace mla_decode_varlen_fwd needs for this shape (0 on bad sizes). */
+size_t mla_decode_varlen_workspace_size(int B, int total, int H, int d, int r, mla_dtype dt);
+
+/* Decode over a packed (variable-length) latent cache: the same computation
+ * as mla_decode_fwd, with sequence b's cached latents in rows
+ * cu_seqlens[b] .. cu_seqlens[b+1]-1 of kv_latent [total, r] instead of a
+ * padded [B, Tmax, r].
+ *   cu_seqlens [B+1] int32 in DEVICE memory, 0 <= cu_seqlens[b] < cu_seqlens[b+1] <= total
+ *   (every sequence non-empty).  The host does not inspect it; out of that
+ *   contract each sequence is clamped into the cache (first row into [0, total),
+ *   length into [1, total - first row]), so no read leaves kv_latent, but the
+ *   result is unspecified.
+ * Everything else as mla_decode_fwd; results are bit-identical to
+ * mla_decode_fwd on the same latents laid out padded. */
+mla_status mla_decode_varlen_fwd(const void* q, const void* kv_latent, const int32_t* cu_seqlens,
+                                 const void* w_up_k, const void* w_up_v, void* out, int B, int total,
+                                 int H, int d, int r, float scale, mla_dtype dt, void* workspace,
+                                 size_t workspace_bytes, void* stream);
+
+/* Append one latent per sequence to a padded decode cache, on the device:
+ *   kv_cache [B, Tmax, r] (in/out), seq_lens [B] int32 DEVICE (in/out),
+ *   new_latent [B, r] (e.g. from mla_down_proj of the new token).
+ * For each b with 0 <= seq_lens[b] < Tmax: kv_cache[b, seq_lens[b], :] =
+ * new_latent[b, :], then seq_lens[b] += 1.  A sequence whose cache is full
+ * (or whose length is outside [0, Tmax)) is left unchanged; nothing else of
+ * the cache is written.  The lengths stay on the device, so a decode step
+ * (append, then mla_decode_fwd) needs no host round trip.  The position the
+ * token is written to is the cache length before the call; it becomes part
+ * of the attended keys of the following decode. */
+mla_status mla_kv_append(void* kv_cache, int32_t* seq_lens, const void* new_latent, int B, int Tmax,
+                         int r, mla_dtype dt, void* stream);
+
 /* Per-kernel timing, for benchmarking (not part of the computation).
  * mla_profile_enable(1) makes every later kernel launch of the library record
  * a pair of HIP events on its stream; mla_profile_enable(0) stops it.

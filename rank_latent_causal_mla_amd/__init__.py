@@ -20,7 +20,8 @@ MLA_DTYPE_F32, MLA_DTYPE_BF16 = 0, 1
 
 EXPORTED = ("mla_down_proj", "mla_latent_attn_workspace_size", "mla_latent_attn_fwd",
             "mla_latent_attn_unabsorbed_workspace_size", "mla_latent_attn_fwd_unabsorbed",
-            "mla_decode_workspace_size", "mla_decode_fwd", "mla_profile_enable", "mla_profile_collect",
+            "mla_decode_workspace_size", "mla_decode_fwd", "mla_decode_varlen_workspace_size",
+            "mla_decode_varlen_fwd", "mla_kv_append", "mla_profile_enable", "mla_profile_collect",
             "mla_status_string", "mla_last_error")
 
 _lib = None
@@ -55,6 +56,12 @@ def load():
     lib.mla_decode_workspace_size.argtypes = [i32] * 6
     lib.mla_decode_fwd.restype = i32
     lib.mla_decode_fwd.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, i32, vp, sz, vp]
+    lib.mla_decode_varlen_workspace_size.restype = sz
+    lib.mla_decode_varlen_workspace_size.argtypes = [i32] * 6
+    lib.mla_decode_varlen_fwd.restype = i32
+    lib.mla_decode_varlen_fwd.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, i32, vp, sz, vp]
+    lib.mla_kv_append.restype = i32
+    lib.mla_kv_append.argtypes = [vp, vp, vp, i32, i32, i32, i32, vp]
     lib.mla_status_string.restype = ctypes.c_char_p
     lib.mla_status_string.argtypes = [i32]
     lib.mla_last_error.restype = ctypes.c_char_p
@@ -114,6 +121,20 @@ def mla_decode_fwd_raw(q, kv_latent, seq_lens, w_up_k, w_up_v, out, B, Tmax, H, 
                        ws_bytes, stream=0):
     return load().mla_decode_fwd(q, kv_latent, seq_lens, w_up_k, w_up_v, out, B, Tmax, H, d, r, scale, dt, ws,
                                  ws_bytes, stream)
+
+
+def mla_decode_varlen_workspace_size(B, total, H, d, r, dt):
+    return int(load().mla_decode_varlen_workspace_size(B, total, H, d, r, dt))
+
+
+def mla_decode_varlen_fwd_raw(q, kv_latent, cu_seqlens, w_up_k, w_up_v, out, B, total, H, d, r, scale, dt, ws,
+                              ws_bytes, stream=0):
+    return load().mla_decode_varlen_fwd(q, kv_latent, cu_seqlens, w_up_k, w_up_v, out, B, total, H, d, r, scale,
+                                        dt, ws, ws_bytes, stream)
+
+
+def mla_kv_append_raw(kv_cache, seq_lens, new_latent, B, Tmax, r, dt, stream=0):
+    return load().mla_kv_append(kv_cache, seq_lens, new_latent, B, Tmax, r, dt, stream)
 
 
 def mla_profile_enable(on: bool = True):
@@ -236,6 +257,47 @@ def mla_decode_fwd(q, kv_latent, seq_lens, w_up_k, w_up_v, out=None, scale=None,
                               workspace.data_ptr(), workspace.numel() * workspace.element_size(),
                               _stream(stream)))
     return out
+
+
+def mla_decode_varlen_fwd(q, kv_latent, cu_seqlens, w_up_k, w_up_v, out=None, scale=None, workspace=None,
+                          stream=None):
+    """Decode over a packed cache: q[B,1,H,d], kv_latent[total,r], cu_seqlens[B+1] int32 (device) -> out[B,1,H,d]."""
+    import torch
+    _dev(q, kv_latent, cu_seqlens, w_up_k, w_up_v)
+    if cu_seqlens.dtype != torch.int32 or not cu_seqlens.is_contiguous():
+        raise ValueError("cu_seqlens must be contiguous int32")
+    B, _, H, d = q.shape
+    total, r = kv_latent.shape
+    if cu_seqlens.numel() != B + 1:
+        raise ValueError("cu_seqlens needs B + 1 entries")
+    dt = _dt(q)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    nbytes = mla_decode_varlen_workspace_size(B, total, H, d, r, dt)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    _dev(out, workspace)
+    _check(mla_decode_varlen_fwd_raw(q.data_ptr(), kv_latent.data_ptr(), cu_seqlens.data_ptr(), w_up_k.data_ptr(),
+                                     w_up_v.data_ptr(), out.data_ptr(), B, total, H, d, r, float(scale), dt,
+                                     workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                                     _stream(stream)))
+    return out
+
+
+def mla_kv_append(kv_cache, seq_lens, new_latent, stream=None):
+    """kv_cache[B,Tmax,r] and seq_lens[B] int32 (device) updated in place with new_latent[B,r]."""
+    import torch
+    _dev(kv_cache, seq_lens, new_latent)
+    if seq_lens.dtype != torch.int32 or not seq_lens.is_contiguous():
+        raise ValueError("seq_lens must be contiguous int32")
+    B, Tmax, r = kv_cache.shape
+    if tuple(new_latent.shape) != (B, r) or new_latent.dtype != kv_cache.dtype:
+        raise ValueError("new_latent must be [B, r] in the cache's dtype")
+    _check(mla_kv_append_raw(kv_cache.data_ptr(), seq_lens.data_ptr(), new_latent.data_ptr(), B, Tmax, r,
+                             _dt(kv_cache), _stream(stream)))
+    return kv_cache
 
 
 def full_path(hidden, w_down, q, w_up_k, w_up_v, scale=None, stream=None):

@@ -60,8 +60,8 @@ __device__ __forceinline__ int decode_chunk(int N, int P) {
 template <int R>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
 void decode_split(const uint16_t* __restrict__ q_lat, const uint16_t* __restrict__ lat,
-                  const int32_t* __restrict__ S, uint16_t* __restrict__ part_o,
-                  float* __restrict__ part_ml, int B, int Tmax, int H, int P) {
+                  const int32_t* __restrict__ S, const int32_t* __restrict__ RB, uint16_t* __restrict__ part_o,
+                  float* __restrict__ part_ml, int B, int H, int P) {
   constexpr int TILE = kDecodeTileKeys * R * 2;
   constexpr int NI = TILE / 1024 / 4;  // copy instructions per wave and tile
   constexpr int NKS = R / 32;          // contraction steps of a score block
@@ -104,7 +104,8 @@ void decode_split(const uint16_t* __restrict__ q_lat, const uint16_t* __restrict
   bool ddone = false;
   int issued = 0;
   auto copy_next = [&]() {
-    dma_tile32<R>(lat + (size_t)db * Tmax * R, dk, dend, lds0 + (issued % kDecodeBufs) * TILE, w);
+    const int rb = __builtin_amdgcn_readfirstlane(RB[db]);  // first cache row of sequence db
+    dma_tile32<R>(lat + (size_t)rb * R, dk, dend, lds0 + (issued % kDecodeBufs) * TILE, w);
     ++issued;
     dk += kDecodeTileKeys;
     if (dk >= dend) {
@@ -283,19 +284,20 @@ void decode_split(const uint16_t* __restrict__ q_lat, const uint16_t* __restrict
 }
 
 // Prologue of a decode call in one launch (independent block roles):
-//   block 0                  -- the prefix S of the clamped lengths;
+//   block 0                  -- the prefix S of the clamped lengths and the row bases RB;
 //   the next nabs blocks     -- absorption, 32 sequences x 128 rho of one head each;
 //   the last ntr blocks      -- the W_uv transpose, 64 x 64 tiles.
 template <int R, int DK>
 __global__ __launch_bounds__(256) void decode_prep(const uint16_t* __restrict__ q, const uint16_t* __restrict__ wk,
                                                    uint16_t* __restrict__ q_lat, const uint16_t* __restrict__ wv,
                                                    uint16_t* __restrict__ wvT, const int32_t* __restrict__ lens,
-                                                   int B, int Tmax, int H, int d, float qscale,
-                                                   int32_t* __restrict__ S, int nabs) {
+                                                   const int32_t* __restrict__ cu, int B, int Tmax, int H, int d,
+                                                   float qscale, int32_t* __restrict__ S, int32_t* __restrict__ RB,
+                                                   int nabs) {
   constexpr int NQ = R / 128;
   const int bid = blockIdx.x;
   if (bid == 0) {
-    length_prefix_block(lens, B, Tmax, S);
+    length_prefix_block(lens, cu, B, Tmax, S, RB);
   } else if (bid <= nabs) {
     const int t = bid - 1;
     absorb_tile<R, DK, 1>(q, wk, q_lat, B, H, qscale, t / (H * NQ), 1, (t / NQ) % H, 128 * (t % NQ));
@@ -445,10 +447,10 @@ static int device_cus() {
 size_t decode_max_splits(int B) { return (size_t)decode_split_cap() + B; }
 
 template <int R>
-static hipError_t run_decode(const uint16_t* q, const uint16_t* lat, const int32_t* lens,
+static hipError_t run_decode(const uint16_t* q, const uint16_t* lat, const int32_t* lens, const int32_t* cu,
                              const uint16_t* wk, const uint16_t* wv, uint16_t* out, int B, int Tmax,
                              int H, int d, float sl2, uint16_t* q_lat, uint16_t* part_o, float* part_ml,
-                             uint16_t* wvT, int32_t* S, hipStream_t st) {
+                             uint16_t* wvT, int32_t* S, int32_t* RB, hipStream_t st) {
   // one chunk of keys per compute unit over all head groups
   const int nhg = (H + 31) / 32;
   int P = device_cus() / nhg;
@@ -467,8 +469,8 @@ static hipError_t run_decode(const uint16_t* q, const uint16_t* lat, const int32
     const int ntr = (R / kTransposeTile) * ((d + kTransposeTile - 1) / kTransposeTile) * H;
     const dim3 grid(1 + nabs + ntr);
 #define PREP(DK)                                                                                          \
-  hipLaunchKernelGGL((decode_prep<R, DK>), grid, dim3(256), 0, st, q, wk, q_lat, wv, wvT, lens, B, Tmax, H, d, \
-                     sl2, S, nabs)
+  hipLaunchKernelGGL((decode_prep<R, DK>), grid, dim3(256), 0, st, q, wk, q_lat, wv, wvT, lens, cu, B, Tmax, H, \
+                     d, sl2, S, RB, nabs)
     switch (d) {
       case 32: PREP(2); break;
       case 64: PREP(4); break;
@@ -480,8 +482,8 @@ static hipError_t run_decode(const uint16_t* q, const uint16_t* lat, const int32
   }
   {
     ProfScope ps("decode_split", st);
-    hipLaunchKernelGGL(decode_split<R>, dim3(P, nhg), dim3(256), lds, st, q_lat, lat, S, part_o, part_ml, B, Tmax,
-                       H, P);
+    hipLaunchKernelGGL(decode_split<R>, dim3(P, nhg), dim3(256), lds, st, q_lat, lat, S, RB, part_o, part_ml, B, H,
+                       P);
   }
   {
     ProfScope ps("decode_merge_up", st);
@@ -492,7 +494,7 @@ static hipError_t run_decode(const uint16_t* q, const uint16_t* lat, const int32
 }
 
 // Workspace: q_lat [B*H][r] bf16 | W_uv^T [H][d][r] | partial o [M][H][r] bf16 |
-// partial (m, l) [M][H][2] f32 | length prefix [B + 1] int32, with
+// partial (m, l) [M][H][2] f32 | length prefix [B + 1] int32 | row bases [B] int32, with
 // M = decode_split_cap() + B partial slots; each part 256-byte aligned.
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
@@ -503,11 +505,11 @@ size_t decode_mfma_workspace(int B, int Tmax, int H, int d, int r) {
   bytes = align256(bytes + (size_t)H * d * r * 2);
   bytes = align256(bytes + M * H * r * 2);
   bytes = align256(bytes + M * H * 2 * 4);
-  bytes += (size_t)(B + 1) * 4;
+  bytes += (size_t)(B + 1) * 4 + (size_t)B * 4;
   return bytes;
 }
 
-hipError_t decode_mfma(const void* q, const void* lat, const int32_t* lens, const void* wk,
+hipError_t decode_mfma(const void* q, const void* lat, const int32_t* lens, const int32_t* cu, const void* wk,
                        const void* wv, void* out, int B, int Tmax, int H, int d, int r, float sl2,
                        void* ws, hipStream_t st) {
   const size_t M = decode_max_splits(B);
@@ -521,8 +523,9 @@ hipError_t decode_mfma(const void* q, const void* lat, const int32_t* lens, cons
   float* part_ml = (float*)(p + off);
   off = align256(off + M * H * 2 * 4);
   int32_t* S = (int32_t*)(p + off);
-#define ARGS (const uint16_t*)q, (const uint16_t*)lat, lens, (const uint16_t*)wk, (const uint16_t*)wv, \
-             (uint16_t*)out, B, Tmax, H, d, sl2, q_lat, part_o, part_ml, wvT, S, st
+  int32_t* RB = S + B + 1;
+#define ARGS (const uint16_t*)q, (const uint16_t*)lat, lens, cu, (const uint16_t*)wk, (const uint16_t*)wv, \
+             (uint16_t*)out, B, Tmax, H, d, sl2, q_lat, part_o, part_ml, wvT, S, RB, st
   switch (r) {
     case 128: return run_decode<128>(ARGS);
     case 256: return run_decode<256>(ARGS);

@@ -40,11 +40,13 @@ __global__ void absorb_simt(const T* __restrict__ q, const T* __restrict__ wk,
 
 // Streaming-softmax attention of one query row per wave over the latents.
 // Prefill: row = (b*T + t)*H + h attends keys 0..t of batch b.
-// Decode:  row = b*H + h attends keys 0..L_b-1 (L_b = seq_lens[b] clamped to [1, Tl]).
+// Decode:  row = b*H + h attends keys 0..L_b-1 (L_b = seq_lens[b] clamped to [1, Tl]) of a
+//          padded cache [B, Tl, R]; with cu, the rows cu[b] .. cu[b+1]-1 of a packed cache
+//          [Tl, R] (clamped into the cache, as the matrix-core path does).
 template <typename T, bool DECODE>
 __global__ void attend_simt(const float* __restrict__ q_lat, const T* __restrict__ lat,
-                            const int32_t* __restrict__ lens, float* __restrict__ o_lat,
-                            int Tl, int H, int R, float sl2, long nrows) {
+                            const int32_t* __restrict__ lens, const int32_t* __restrict__ cu,
+                            float* __restrict__ o_lat, int Tl, int H, int R, float sl2, long nrows) {
   __shared__ float qs[4][1024];
   __shared__ float ps[4][64];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -52,13 +54,23 @@ __global__ void attend_simt(const float* __restrict__ q_lat, const T* __restrict
   if (row >= nrows) return;  // whole wave; no block-level barrier below
   long b;
   int nkeys;
-  if (DECODE) {
+  size_t base;  // first cache row of the sequence
+  if (DECODE && cu) {
+    b = row / H;
+    const int c0 = cu[b], c1 = cu[b + 1];
+    const int rb = c0 < 0 ? 0 : (c0 > Tl - 1 ? Tl - 1 : c0);
+    const int L = c1 - c0, Lmax = Tl - rb;
+    nkeys = L < 1 ? 1 : (L > Lmax ? Lmax : L);
+    base = (size_t)rb;
+  } else if (DECODE) {
     b = row / H;
     int L = lens[b];
     nkeys = L < 1 ? 1 : (L > Tl ? Tl : L);
+    base = (size_t)b * Tl;
   } else {
     b = row / ((long)Tl * H);
     nkeys = (int)((row / H) % Tl) + 1;
+    base = (size_t)b * Tl;
   }
   for (int rho = lane; rho < R; rho += 64) qs[w][rho] = q_lat[row * R + rho];
   __builtin_amdgcn_wave_barrier();
@@ -66,7 +78,7 @@ __global__ void attend_simt(const float* __restrict__ q_lat, const T* __restrict
 #pragma unroll
   for (int i = 0; i < 16; ++i) o[i] = 0.f;
   float m = -INFINITY, l = 0.f;
-  const T* latb = lat + (size_t)b * Tl * R;
+  const T* latb = lat + base * R;
   for (int s0 = 0; s0 < nkeys; s0 += 64) {
     const int s = s0 + lane;
     float x = -INFINITY;
@@ -173,7 +185,7 @@ static hipError_t prefill_simt_t(const T* q, const T* lat, const T* wk, const T*
   }
   {
     ProfScope ps("attend_simt", st);
-    hipLaunchKernelGGL((attend_simt<T, false>), dim3((rows + 3) / 4), dim3(256), 0, st, q_lat, lat,
+    hipLaunchKernelGGL((attend_simt<T, false>), dim3((rows + 3) / 4), dim3(256), 0, st, q_lat, lat, nullptr,
                        (const int32_t*)nullptr, o_lat, T_, H, r, sl2, rows);
   }
   {
@@ -184,7 +196,7 @@ static hipError_t prefill_simt_t(const T* q, const T* lat, const T* wk, const T*
 }
 
 template <typename T>
-static hipError_t decode_simt_t(const T* q, const T* lat, const int32_t* lens, const T* wk,
+static hipError_t decode_simt_t(const T* q, const T* lat, const int32_t* lens, const int32_t* cu, const T* wk,
                                 const T* wv, T* out, int B, int Tmax, int H, int d, int r,
                                 float sl2, void* ws, hipStream_t st) {
   const long rows = (long)B * H;
@@ -197,7 +209,7 @@ static hipError_t decode_simt_t(const T* q, const T* lat, const int32_t* lens, c
   {
     ProfScope ps("attend_simt", st);
     hipLaunchKernelGGL((attend_simt<T, true>), dim3((rows + 3) / 4), dim3(256), 0, st, q_lat, lat,
-                       lens, o_lat, Tmax, H, r, sl2, rows);
+                       lens, cu, o_lat, Tmax, H, r, sl2, rows);
   }
   {
     ProfScope ps("up_simt", st);
@@ -224,15 +236,45 @@ size_t prefill_simt_workspace(int B, int T, int H, int d, int r) {
   return (size_t)2 * B * T * H * r * sizeof(float);
 }
 
-hipError_t decode_simt(bool bf16, const void* q, const void* lat, const int32_t* lens,
+hipError_t decode_simt(bool bf16, const void* q, const void* lat, const int32_t* lens, const int32_t* cu,
                        const void* wk, const void* wv, void* out, int B, int Tmax, int H, int d,
                        int r, float scale, void* ws, hipStream_t st) {
   const float sl2 = scale * kLog2e;
   if (bf16)
-    return decode_simt_t((const uint16_t*)q, (const uint16_t*)lat, lens, (const uint16_t*)wk,
+    return decode_simt_t((const uint16_t*)q, (const uint16_t*)lat, lens, cu, (const uint16_t*)wk,
                          (const uint16_t*)wv, (uint16_t*)out, B, Tmax, H, d, r, sl2, ws, st);
-  return decode_simt_t((const float*)q, (const float*)lat, lens, (const float*)wk,
+  return decode_simt_t((const float*)q, (const float*)lat, lens, cu, (const float*)wk,
                        (const float*)wv, (float*)out, B, Tmax, H, d, r, sl2, ws, st);
+}
+
+// One block per sequence: row lens[b] of kv_cache[b] takes new_latent[b], then
+// lens[b] grows by one; a sequence whose cache is full (or whose length is
+// outside [0, Tmax)) is left unchanged.
+template <typename T>
+__global__ void kv_append_kernel(T* __restrict__ kv_cache, int32_t* __restrict__ lens,
+                                 const T* __restrict__ new_latent, int Tmax, int r) {
+  __shared__ int pos;
+  const int b = blockIdx.x;
+  if (threadIdx.x == 0) pos = lens[b];
+  __syncthreads();
+  const int p = pos;
+  if (p < 0 || p >= Tmax) return;  // whole block
+  T* dst = kv_cache + ((size_t)b * Tmax + p) * r;
+  const T* src = new_latent + (size_t)b * r;
+  for (int i = threadIdx.x; i < r; i += blockDim.x) dst[i] = src[i];
+  if (threadIdx.x == 0) lens[b] = p + 1;
+}
+
+hipError_t kv_append(bool bf16, void* kv_cache, int32_t* lens, const void* new_latent, int B, int Tmax, int r,
+                     hipStream_t st) {
+  ProfScope ps("kv_append", st);
+  if (bf16)
+    hipLaunchKernelGGL(kv_append_kernel<uint16_t>, dim3(B), dim3(256), 0, st, (uint16_t*)kv_cache, lens,
+                       (const uint16_t*)new_latent, Tmax, r);
+  else
+    hipLaunchKernelGGL(kv_append_kernel<float>, dim3(B), dim3(256), 0, st, (float*)kv_cache, lens,
+                       (const float*)new_latent, Tmax, r);
+  return hipGetLastError();
 }
 
 size_t decode_simt_workspace(int B, int Tmax, int H, int d, int r) {

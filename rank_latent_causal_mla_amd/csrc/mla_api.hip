@@ -179,19 +179,26 @@ size_t mla_decode_workspace_size(int B, int Tmax, int H, int d, int r, mla_dtype
                             : mla::decode_simt_workspace(B, Tmax, H, d, r);
 }
 
-mla_status mla_decode_fwd(const void* q, const void* kv_latent, const int32_t* seq_lens,
-                          const void* w_up_k, const void* w_up_v, void* out, int B, int Tmax,
-                          int H, int d, int r, float scale, mla_dtype dt, void* workspace,
-                          size_t workspace_bytes, void* stream) {
-  if (!q || !kv_latent || !seq_lens || !w_up_k || !w_up_v || !out || !workspace)
+}  // extern "C"
+
+namespace {
+
+// Decode over a padded cache (lens, rows = Tmax per sequence) or a packed one
+// (cu, rows = the cache's total row count).
+mla_status decode_common(const void* q, const void* kv_latent, const int32_t* seq_lens, const int32_t* cu,
+                         const void* w_up_k, const void* w_up_v, void* out, int B, int rows, int H, int d, int r,
+                         float scale, mla_dtype dt, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!q || !kv_latent || !(seq_lens || cu) || !w_up_k || !w_up_v || !out || !workspace)
     return fail(MLA_ERR_INVALID_ARGUMENT, "null pointer");
-  mla_status s = check_dims(B, Tmax, H, d, r, dt, "Tmax");
+  const int32_t* ints = cu ? cu : seq_lens;
+  mla_status s = cu ? check_dims(B, 1, H, d, r, dt, "T") : check_dims(B, rows, H, d, r, dt, "Tmax");
   if (s != MLA_OK) return s;
+  if (cu && rows < 1) return fail(MLA_ERR_INVALID_ARGUMENT, "total must be positive (got %d)", rows);
   if (!std::isfinite(scale)) return fail(MLA_ERR_INVALID_ARGUMENT, "scale must be finite");
   if (!aligned16(q) || !aligned16(kv_latent) || !aligned16(w_up_k) || !aligned16(w_up_v) ||
-      !aligned16(out) || !aligned16(workspace) || ((uintptr_t)seq_lens & 3u))
-    return fail(MLA_ERR_INVALID_ARGUMENT, "pointers must be 16-byte aligned (seq_lens 4-byte)");
-  const size_t need = mla_decode_workspace_size(B, Tmax, H, d, r, dt);
+      !aligned16(out) || !aligned16(workspace) || ((uintptr_t)ints & 3u))
+    return fail(MLA_ERR_INVALID_ARGUMENT, "pointers must be 16-byte aligned (lengths 4-byte)");
+  const size_t need = mla_decode_workspace_size(B, rows, H, d, r, dt);
   if (workspace_bytes < need)
     return fail(MLA_ERR_WORKSPACE, "workspace %zu bytes < %zu required", workspace_bytes, need);
   hipStream_t st = (hipStream_t)stream;
@@ -202,13 +209,54 @@ mla_status mla_decode_fwd(const void* q, const void* kv_latent, const int32_t* s
     if (mla::decode_lds_bytes(r) > limit)
       return fail(MLA_ERR_UNSUPPORTED, "decode needs %zu bytes of LDS per block, device allows %zu",
                   mla::decode_lds_bytes(r), limit);
-    return launched(mla::decode_mfma(q, kv_latent, seq_lens, w_up_k, w_up_v, out, B, Tmax, H, d, r,
+    return launched(mla::decode_mfma(q, kv_latent, seq_lens, cu, w_up_k, w_up_v, out, B, rows, H, d, r,
                                      (float)(scale * kLog2e), workspace, st),
                     "decode launch");
   }
-  return launched(mla::decode_simt(dt == MLA_DTYPE_BF16, q, kv_latent, seq_lens, w_up_k, w_up_v,
-                                   out, B, Tmax, H, d, r, scale, workspace, st),
+  return launched(mla::decode_simt(dt == MLA_DTYPE_BF16, q, kv_latent, seq_lens, cu, w_up_k, w_up_v,
+                                   out, B, rows, H, d, r, scale, workspace, st),
                   "decode launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+mla_status mla_decode_fwd(const void* q, const void* kv_latent, const int32_t* seq_lens,
+                          const void* w_up_k, const void* w_up_v, void* out, int B, int Tmax,
+                          int H, int d, int r, float scale, mla_dtype dt, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  if (!seq_lens) return fail(MLA_ERR_INVALID_ARGUMENT, "null pointer");
+  return decode_common(q, kv_latent, seq_lens, nullptr, w_up_k, w_up_v, out, B, Tmax, H, d, r, scale, dt,
+                       workspace, workspace_bytes, stream);
+}
+
+size_t mla_decode_varlen_workspace_size(int B, int total, int H, int d, int r, mla_dtype dt) {
+  return mla_decode_workspace_size(B, total, H, d, r, dt);
+}
+
+mla_status mla_decode_varlen_fwd(const void* q, const void* kv_latent, const int32_t* cu_seqlens,
+                                 const void* w_up_k, const void* w_up_v, void* out, int B, int total,
+                                 int H, int d, int r, float scale, mla_dtype dt, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+  if (!cu_seqlens) return fail(MLA_ERR_INVALID_ARGUMENT, "null pointer");
+  return decode_common(q, kv_latent, nullptr, cu_seqlens, w_up_k, w_up_v, out, B, total, H, d, r, scale, dt,
+                       workspace, workspace_bytes, stream);
+}
+
+mla_status mla_kv_append(void* kv_cache, int32_t* seq_lens, const void* new_latent, int B, int Tmax, int r,
+                         mla_dtype dt, void* stream) {
+  if (!kv_cache || !seq_lens || !new_latent) return fail(MLA_ERR_INVALID_ARGUMENT, "null pointer");
+  if (B < 1 || Tmax < 1 || r < 1)
+    return fail(MLA_ERR_INVALID_ARGUMENT, "sizes must be positive (B=%d Tmax=%d r=%d)", B, Tmax, r);
+  if (dt != MLA_DTYPE_F32 && dt != MLA_DTYPE_BF16) return fail(MLA_ERR_INVALID_ARGUMENT, "unknown dtype %d", (int)dt);
+  if (!aligned16(kv_cache) || !aligned16(new_latent) || ((uintptr_t)seq_lens & 3u))
+    return fail(MLA_ERR_INVALID_ARGUMENT, "pointers must be 16-byte aligned (seq_lens 4-byte)");
+  if ((double)B * Tmax >= 2147483647.0 || (double)B * Tmax * r >= 9.0e15)
+    return fail(MLA_ERR_UNSUPPORTED, "problem too large");
+  return launched(mla::kv_append(dt == MLA_DTYPE_BF16, kv_cache, seq_lens, new_latent, B, Tmax, r,
+                                 (hipStream_t)stream),
+                  "kv append launch");
 }
 
 }  // extern "C"

@@ -26,7 +26,8 @@ hipError_t prefill_mfma(const void* q, const void* lat, const void* wk, const vo
                         int B, int T, int H, int d, int r, float sl2, void* ws, hipStream_t st);
 size_t prefill_mfma_workspace(int B, int T, int H, int d, int r);
 size_t decode_mfma_workspace(int B, int Tmax, int H, int d, int r);
-hipError_t decode_mfma(const void* q, const void* lat, const int32_t* lens, const void* wk,
+// lens (padded cache [B, Tmax, r]) or cu (packed cache [Tmax = total rows, r]; lens unused)
+hipError_t decode_mfma(const void* q, const void* lat, const int32_t* lens, const int32_t* cu, const void* wk,
                        const void* wv, void* out, int B, int Tmax, int H, int d, int r, float sl2,
                        void* ws, hipStream_t st);
 // q_lat[n*H + h, :] = qscale * W_uk[:, h, :] q[n, h, :] for N tokens (bf16).
@@ -52,10 +53,14 @@ hipError_t prefill_simt(bool dt_bf16, const void* q, const void* lat, const void
                         const void* wv, void* out, int B, int T, int H, int d, int r,
                         float scale, void* ws, hipStream_t st);
 size_t prefill_simt_workspace(int B, int T, int H, int d, int r);
-hipError_t decode_simt(bool dt_bf16, const void* q, const void* lat, const int32_t* lens,
+hipError_t decode_simt(bool dt_bf16, const void* q, const void* lat, const int32_t* lens, const int32_t* cu,
                        const void* wk, const void* wv, void* out, int B, int Tmax, int H, int d,
                        int r, float scale, void* ws, hipStream_t st);
 size_t decode_simt_workspace(int B, int Tmax, int H, int d, int r);
+
+// ---- cache append: kv_cache[b, lens[b], :] = new_latent[b, :], lens[b] += 1 while lens[b] < Tmax
+hipError_t kv_append(bool dt_bf16, void* kv_cache, int32_t* lens, const void* new_latent, int B, int Tmax, int r,
+                     hipStream_t st);
 
 // ---- down-projection (any sizes), float32 accumulation
 hipError_t down_proj(bool dt_bf16, const void* hidden, const void* w_down, void* latent, int M,

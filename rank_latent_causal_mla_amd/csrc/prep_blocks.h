@@ -96,10 +96,26 @@ __device__ __forceinline__ void transpose_wv_tile(const uint16_t* __restrict__ w
 
 __device__ __forceinline__ int clamp_len(int L, int Tmax) { return L < 1 ? 1 : (L > Tmax ? Tmax : L); }
 
-// Exclusive prefix of the clamped decode lengths (one 256-thread block):
-// S[b] = sum_{b' < b} clamp(L_b'), S[B] = the total.
-__device__ __forceinline__ void length_prefix_block(const int32_t* __restrict__ lens, int B, int Tmax,
-                                                    int32_t* __restrict__ S) {
+// Where each decode sequence's latents start and how many it has (one
+// 256-thread block): RB[b] is its first cache row and S the exclusive prefix
+// of the lengths (S[B] = the total).  Padded cache [B, Tmax, r]: RB[b] =
+// b Tmax and the length clamp(lens[b], 1, Tmax).  Packed cache [total, r]
+// (cu != nullptr, `Tmax` = total): RB[b] = clamp(cu[b], 0, total - 1) and the
+// length clamp(cu[b + 1] - cu[b], 1, total - RB[b]), so every row read is a
+// row of the cache whatever cu holds.
+__device__ __forceinline__ void length_prefix_block(const int32_t* __restrict__ lens,
+                                                    const int32_t* __restrict__ cu, int B, int Tmax,
+                                                    int32_t* __restrict__ S, int32_t* __restrict__ RB) {
+  auto len = [&](int b) {
+    if (!cu) {
+      RB[b] = b * Tmax;
+      return clamp_len(lens[b], Tmax);
+    }
+    const int c0 = cu[b], c1 = cu[b + 1];
+    const int base = c0 < 0 ? 0 : (c0 > Tmax - 1 ? Tmax - 1 : c0);
+    RB[b] = base;
+    return clamp_len(c1 - c0, Tmax - base);
+  };
   __shared__ int scan[256];
   __shared__ int carry;
   const int tid = threadIdx.x;
@@ -107,7 +123,7 @@ __device__ __forceinline__ void length_prefix_block(const int32_t* __restrict__ 
   __syncthreads();
   for (int b0 = 0; b0 < B; b0 += 256) {
     const int b = b0 + tid;
-    const int L = b < B ? clamp_len(lens[b], Tmax) : 0;
+    const int L = b < B ? len(b) : 0;
     scan[tid] = L;
     __syncthreads();
     for (int o = 1; o < 256; o <<= 1) {  // inclusive Hillis-Steele scan

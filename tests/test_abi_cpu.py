@@ -104,6 +104,48 @@ def test_unabsorbed_workspace_size():
     assert mla.mla_latent_attn_unabsorbed_workspace_size(2, 64, 4, 64, 512, BF16) == 0
 
 
+def varlen(**kw):
+    a = dict(q=P, kv=P, cu=P, wk=P, wv=P, out=P, B=2, total=100, H=4, d=32, r=32, scale=0.17, dt=F32, ws=P,
+             wsb=1 << 40)
+    a.update(kw)
+    return mla.mla_decode_varlen_fwd_raw(a["q"], a["kv"], a["cu"], a["wk"], a["wv"], a["out"], a["B"], a["total"],
+                                         a["H"], a["d"], a["r"], a["scale"], a["dt"], a["ws"], a["wsb"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    ({"cu": 0}, mla.MLA_ERR_INVALID_ARGUMENT),
+    ({"cu": P + 2}, mla.MLA_ERR_INVALID_ARGUMENT),
+    ({"q": 0}, mla.MLA_ERR_INVALID_ARGUMENT),
+    ({"total": 0}, mla.MLA_ERR_INVALID_ARGUMENT),
+    ({"B": 0}, mla.MLA_ERR_INVALID_ARGUMENT),
+    ({"dt": 5}, mla.MLA_ERR_INVALID_ARGUMENT),
+    ({"r": 2048}, mla.MLA_ERR_UNSUPPORTED),
+    ({"wsb": 3}, mla.MLA_ERR_WORKSPACE),
+])
+def test_varlen_argument_errors(kw, status):
+    assert varlen(**kw) == status
+    assert mla.last_error() != ""
+
+
+def test_varlen_workspace_matches_padded():
+    for dt in (F32, BF16):
+        assert mla.mla_decode_varlen_workspace_size(64, 300000, 32, 128, 512, dt) == \
+            mla.mla_decode_workspace_size(64, 300000, 32, 128, 512, dt) > 0
+
+
+@pytest.mark.parametrize("args,status", [
+    ((0, P, P, 2, 8, 32, F32), mla.MLA_ERR_INVALID_ARGUMENT),     # null cache
+    ((P, 0, P, 2, 8, 32, F32), mla.MLA_ERR_INVALID_ARGUMENT),     # null lengths
+    ((P, P + 2, P, 2, 8, 32, F32), mla.MLA_ERR_INVALID_ARGUMENT), # misaligned lengths
+    ((P, P, P, 0, 8, 32, F32), mla.MLA_ERR_INVALID_ARGUMENT),
+    ((P, P, P, 2, 8, 0, BF16), mla.MLA_ERR_INVALID_ARGUMENT),
+    ((P, P, P, 2, 8, 32, 9), mla.MLA_ERR_INVALID_ARGUMENT),
+])
+def test_kv_append_argument_errors(args, status):
+    assert mla.mla_kv_append_raw(*args) == status
+    assert mla.last_error() != ""
+
+
 def test_decode_null_lengths():
     assert dec(lens=0) == mla.MLA_ERR_INVALID_ARGUMENT
     assert dec(lens=P + 2) == mla.MLA_ERR_INVALID_ARGUMENT
