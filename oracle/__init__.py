@@ -44,6 +44,11 @@ def _bind(lib):
     lib.oracle_attend_rows.restype = i32
     lib.oracle_attend_rows.argtypes = [vp, i32, L, vp, vp, vp, vp, i32, L, L, vp, vp, i32,
                                        L, L, L, dbl, vp, vp, L, i32]
+    lib.oracle_attend_rows_masked.restype = i32
+    lib.oracle_attend_rows_masked.argtypes = [vp, i32, L, vp, vp, vp, vp, i32, L, L, vp, vp, i32,
+                                              L, L, L, dbl, vp, vp, vp, L, i32]
+    lib.oracle_latent_attn_masked.restype = i32
+    lib.oracle_latent_attn_masked.argtypes = [vp, i32, vp, i32, vp, vp, i32, L, L, L, L, L, dbl, vp, vp, i32]
     lib.oracle_latent_attn.restype = i32
     lib.oracle_latent_attn.argtypes = [vp, i32, vp, i32, vp, vp, i32, L, L, L, L, L, dbl, vp, i32]
     lib.oracle_decode.restype = i32
@@ -90,8 +95,18 @@ def down_proj(hidden, w_down, lib=None):
     return out
 
 
-def latent_attn(q, kv_latent, w_up_k, w_up_v, scale, nthreads=0, lib=None):
-    """Causal prefill: q [B,T,H,d], kv_latent [B,T,r], w [r,H,d] -> float64 [B,T,H,d]."""
+def _mask(key_mask, shape):
+    if key_mask is None:
+        return None
+    m = np.ascontiguousarray(key_mask, dtype=np.uint8)
+    assert m.shape == shape, (m.shape, shape)
+    return m
+
+
+def latent_attn(q, kv_latent, w_up_k, w_up_v, scale, key_mask=None, nthreads=0, lib=None):
+    """Causal prefill: q [B,T,H,d], kv_latent [B,T,r], w [r,H,d] -> float64 [B,T,H,d].
+    key_mask [B,T] (optional, 0 = masked): masked keys get logit -inf; a row
+    with no unmasked key is NaN."""
     lib = lib or load()
     q, dq = _arr(q)
     lat, dl = _arr(kv_latent)
@@ -102,13 +117,19 @@ def latent_attn(q, kv_latent, w_up_k, w_up_v, scale, nthreads=0, lib=None):
     r = lat.shape[-1]
     assert lat.shape == (B, T, r) and wk.shape == (r, H, d) and wv.shape == (r, H, d)
     out = np.empty((B, T, H, d), dtype=np.float64)
-    _check(lib.oracle_latent_attn(q.ctypes.data, dq, lat.ctypes.data, dl, wk.ctypes.data, wv.ctypes.data, dw,
-                                  B, T, H, d, r, float(scale), out.ctypes.data, nthreads), "latent_attn")
+    m = _mask(key_mask, (B, T))
+    if m is None:
+        _check(lib.oracle_latent_attn(q.ctypes.data, dq, lat.ctypes.data, dl, wk.ctypes.data, wv.ctypes.data, dw,
+                                      B, T, H, d, r, float(scale), out.ctypes.data, nthreads), "latent_attn")
+    else:
+        _check(lib.oracle_latent_attn_masked(q.ctypes.data, dq, lat.ctypes.data, dl, wk.ctypes.data,
+                                             wv.ctypes.data, dw, B, T, H, d, r, float(scale), m.ctypes.data,
+                                             out.ctypes.data, nthreads), "latent_attn_masked")
     return out
 
 
 def attend_rows(q_rows, row_b, row_h, row_nkeys, kv_latent, w_up_k, w_up_v, scale,
-                want_probs=False, nthreads=0, lib=None):
+                want_probs=False, key_mask=None, nthreads=0, lib=None):
     """Rows i of q_rows [n, d] (batch row_b[i], head row_h[i]) attending key
     positions 0 .. row_nkeys[i]-1 of kv_latent [B, Tlat, r].  Returns float64
     out [n, d] (and probs [n, max nkeys], zero beyond each row's keys)."""
@@ -126,10 +147,12 @@ def attend_rows(q_rows, row_b, row_h, row_nkeys, kv_latent, w_up_k, w_up_v, scal
     out = np.empty((n, d), dtype=np.float64)
     pstride = int(rk.max()) if (want_probs and n) else 0
     probs = np.zeros((n, max(pstride, 1)), dtype=np.float64) if want_probs else None
-    _check(lib.oracle_attend_rows(q.ctypes.data, dq, n, rb.ctypes.data, rh.ctypes.data, rk.ctypes.data,
-                                  lat.ctypes.data, dl, B, Tlat, wk.ctypes.data, wv.ctypes.data, dw,
-                                  H, d, r, float(scale), out.ctypes.data,
-                                  probs.ctypes.data if want_probs else None, pstride, nthreads), "attend_rows")
+    m = _mask(key_mask, (B, Tlat))
+    _check(lib.oracle_attend_rows_masked(q.ctypes.data, dq, n, rb.ctypes.data, rh.ctypes.data, rk.ctypes.data,
+                                         lat.ctypes.data, dl, B, Tlat, wk.ctypes.data, wv.ctypes.data, dw,
+                                         H, d, r, float(scale), None if m is None else m.ctypes.data,
+                                         out.ctypes.data, probs.ctypes.data if want_probs else None, pstride,
+                                         nthreads), "attend_rows")
     return (out, probs) if want_probs else out
 
 

@@ -25,6 +25,14 @@
 // Decode: one query per sequence at position L_b - 1, attending the L_b
 // cached latents 0 .. L_b - 1 (the same causal definition for its last row).
 //
+// Key mask (optional, [B, Tlat] bytes, 0 = masked): a masked key's logit is
+// -infinity before the softmax, as the MSA page's attention fills masked
+// scores with -inf ahead of its softmax (page Kimi-K2.6 l2_p29, its model
+// walk-through and its analysis of rows whose every key is masked).  The
+// same two-pass softmax then gives weight 0 to masked keys, and a row with no
+// unmasked key gets NaN weights (-inf - -inf), hence a NaN output, which is
+// what that softmax produces.
+//
 // Inputs are read from their stored bits (float32, bf16 or float64) and
 // widened exactly to double; every sum runs in ascending index order in
 // double; results are returned in double.
@@ -59,6 +67,7 @@ struct Problem {
   const long* row_b; const long* row_h; const long* row_nkeys;
   double* out;                        // [n, d]
   double* probs; long pstride;        // optional [n, pstride]
+  const uint8_t* key_mask;            // optional [B, Tlat], 0 = masked
 };
 
 // One (b, h) pair: materialise k and v for the key positions needed, then
@@ -89,6 +98,7 @@ void attend_group(const Problem& P, const std::vector<long>& rows) {
       double dot = 0.0;
       for (long e = 0; e < d; ++e) dot += load(P.q, P.dt_q, (size_t)i * d + e) * k[s * d + e];
       logit[s] = dot * P.scale;
+      if (P.key_mask && !P.key_mask[(size_t)b * P.Tlat + s]) logit[s] = -INFINITY;
     }
     double m = logit[0];
     for (long s = 1; s < n; ++s) m = std::max(m, logit[s]);
@@ -137,12 +147,12 @@ int oracle_down_proj(const void* hidden, int dt_hidden, const void* w_down, int 
 // 0 .. row_nkeys[i]-1 of kv_latent[row_b[i]] (row_nkeys = t + 1 for prefill
 // position t, = L_b for decode).  out[i, :] receives the attention output;
 // probs (optional, stride pstride >= max nkeys) the softmax weights.
-int oracle_attend_rows(const void* q_rows, int dt_q, long n,
-                       const long* row_b, const long* row_h, const long* row_nkeys,
-                       const void* kv_latent, int dt_lat, long B, long Tlat,
-                       const void* w_up_k, const void* w_up_v, int dt_w,
-                       long H, long d, long r, double scale,
-                       double* out, double* probs, long pstride, int nthreads) {
+int oracle_attend_rows_masked(const void* q_rows, int dt_q, long n,
+                              const long* row_b, const long* row_h, const long* row_nkeys,
+                              const void* kv_latent, int dt_lat, long B, long Tlat,
+                              const void* w_up_k, const void* w_up_v, int dt_w,
+                              long H, long d, long r, double scale, const uint8_t* key_mask,
+                              double* out, double* probs, long pstride, int nthreads) {
   if (n < 0 || B < 1 || Tlat < 1 || H < 1 || d < 1 || r < 1) return 1;
   if (n == 0) return 0;
   if (!q_rows || !row_b || !row_h || !row_nkeys || !kv_latent || !w_up_k || !w_up_v || !out) return 1;
@@ -152,7 +162,7 @@ int oracle_attend_rows(const void* q_rows, int dt_q, long n,
     if (probs && row_nkeys[i] > pstride) return 1;
   }
   Problem P{q_rows, dt_q, kv_latent, dt_lat, w_up_k, w_up_v, dt_w, Tlat, H, d, r, scale,
-            row_b, row_h, row_nkeys, out, probs, pstride};
+            row_b, row_h, row_nkeys, out, probs, pstride, key_mask};
   // group rows by (b, h): each group materialises its k and v once
   std::vector<long> order(n);
   for (long i = 0; i < n; ++i) order[i] = i;
@@ -177,6 +187,35 @@ int oracle_attend_rows(const void* q_rows, int dt_q, long n,
   worker();
   for (auto& th : pool) th.join();
   return 0;
+}
+
+int oracle_attend_rows(const void* q_rows, int dt_q, long n,
+                       const long* row_b, const long* row_h, const long* row_nkeys,
+                       const void* kv_latent, int dt_lat, long B, long Tlat,
+                       const void* w_up_k, const void* w_up_v, int dt_w,
+                       long H, long d, long r, double scale,
+                       double* out, double* probs, long pstride, int nthreads) {
+  return oracle_attend_rows_masked(q_rows, dt_q, n, row_b, row_h, row_nkeys, kv_latent, dt_lat, B, Tlat, w_up_k,
+                                   w_up_v, dt_w, H, d, r, scale, nullptr, out, probs, pstride, nthreads);
+}
+
+// Full causal prefill with a key mask (key_mask [B, T] bytes, 0 = masked;
+// nullptr = none): out[b, t, h, :] for every b < B, t < T, h < H.
+int oracle_latent_attn_masked(const void* q, int dt_q, const void* kv_latent, int dt_lat,
+                              const void* w_up_k, const void* w_up_v, int dt_w,
+                              long B, long T, long H, long d, long r, double scale,
+                              const uint8_t* key_mask, double* out, int nthreads) {
+  if (B < 1 || T < 1 || H < 1) return 1;
+  const long n = B * T * H;
+  std::vector<long> rb(n), rh(n), rk(n);
+  for (long b = 0; b < B; ++b)
+    for (long t = 0; t < T; ++t)
+      for (long h = 0; h < H; ++h) {
+        const long i = (b * T + t) * H + h;
+        rb[i] = b; rh[i] = h; rk[i] = t + 1;
+      }
+  return oracle_attend_rows_masked(q, dt_q, n, rb.data(), rh.data(), rk.data(), kv_latent, dt_lat, B, T,
+                                   w_up_k, w_up_v, dt_w, H, d, r, scale, key_mask, out, nullptr, 0, nthreads);
 }
 
 // Full causal prefill: out[b, t, h, :] for every b < B, t < T, h < H.

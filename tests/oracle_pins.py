@@ -18,7 +18,11 @@ plain mathematics fix:
   * max subtraction: huge logits give the v of the arg-max key;
   * decode(L) equals prefill row L-1, and never reads cache rows >= L;
   * down-projection equals a library fp64 matmul;
-  * bf16 inputs are read exactly (same result as the widened float32 values).
+  * bf16 inputs are read exactly (same result as the widened float32 values);
+  * key mask: brute force over the unmasked keys s <= t, NaN for rows with
+    none (the -inf fill then softmax of the MSA page), and the closed form
+    that a row whose only visible key is s outputs v_s;
+  * an all-ones mask changes nothing.
 """
 from __future__ import annotations
 
@@ -239,6 +243,49 @@ def pin_bf16_inputs_exact(lib):
     assert np.array_equal(got, want)
     want64 = oracle.latent_attn(*(widen(x).astype(np.float64) for x in (qb, lb, kb, vb)), scale, lib=lib)
     assert np.array_equal(got, want64)
+
+
+def pin_mask_brute_force(lib):
+    q, lat, wk, wv, scale = _problem(11, 2, 6, 2, 3, 4)
+    rng = np.random.default_rng(5)
+    mask = (rng.random((2, 6)) < 0.6).astype(np.uint8)
+    mask[0, :] = 1
+    mask[0, 2] = 0
+    mask[1, :3] = 0       # rows t < 3 of batch 1 see no key
+    mask[1, 4] = 1
+    got = oracle.latent_attn(q, lat, wk, wv, scale, key_mask=mask, lib=lib)
+    for b in range(2):
+        for h in range(2):
+            k = lat[b] @ wk[:, h, :]
+            v = lat[b] @ wv[:, h, :]
+            for t in range(6):
+                keys = [s for s in range(t + 1) if mask[b, s]]
+                if not keys:
+                    assert np.isnan(got[b, t, h]).all(), (b, t, h)
+                    continue
+                lg = np.array([scale * q[b, t, h] @ k[s] for s in keys])
+                w = np.exp(lg - lg.max())
+                p = w / w.sum()
+                ref = sum(p[i] * v[s] for i, s in enumerate(keys))
+                _close(got[b, t, h], ref, 1e-12, 1e-14, f"masked brute force b={b} t={t} h={h}")
+
+
+def pin_mask_single_visible_key(lib):
+    # keys 0..2 masked: rows 0..2 have no key (NaN); row 3 sees only key 3, so it is v_3 exactly
+    q, lat, wk, wv, scale = _problem(12, 1, 5, 3, 4, 6)
+    mask = np.array([[0, 0, 0, 1, 1]], dtype=np.uint8)
+    got = oracle.latent_attn(q, lat, wk, wv, scale, key_mask=mask, lib=lib)
+    assert np.isnan(got[0, :3]).all()
+    assert np.isfinite(got[0, 3:]).all()
+    for h in range(3):
+        _close(got[0, 3, h], lat[0, 3] @ wv[:, h, :], 1e-13, 1e-15, f"single visible key h={h}")
+
+
+def pin_mask_all_ones_changes_nothing(lib):
+    q, lat, wk, wv, scale = _problem(13, 2, 7, 2, 3, 5)
+    a = oracle.latent_attn(q, lat, wk, wv, scale, lib=lib)
+    b = oracle.latent_attn(q, lat, wk, wv, scale, key_mask=np.ones((2, 7), np.uint8), lib=lib)
+    assert np.array_equal(a, b)
 
 
 PINS = {name: fn for name, fn in globals().items() if name.startswith("pin_")}

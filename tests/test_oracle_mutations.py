@@ -29,6 +29,10 @@ MUTANTS = {
     "down_proj_transposed": ("load(w_down, dt_w, (size_t)i * r + j)", "load(w_down, dt_w, (size_t)j * D + i)"),
     "bf16_widened_wrong": ("<< 16;  // bf16", "<< 15;  // bf16"),
     "decode_length_short": ("rk[b * H + h] = seq_lens[b];", "rk[b * H + h] = seq_lens[b] > 1 ? seq_lens[b] - 1 : 1;"),
+    "mask_ignored": ("if (P.key_mask && !P.key_mask[(size_t)b * P.Tlat + s]) logit[s] = -INFINITY;", ""),
+    "mask_inverted": ("if (P.key_mask && !P.key_mask[(size_t)b * P.Tlat + s])",
+                      "if (P.key_mask && P.key_mask[(size_t)b * P.Tlat + s])"),
+    "mask_wrong_batch": ("P.key_mask[(size_t)b * P.Tlat + s]", "P.key_mask[(size_t)0 * P.Tlat + s]"),
 }
 
 
