@@ -72,6 +72,17 @@ def prefill_flops(cfg) -> dict:
     return {"absorb": absorb, "attn": attn, "up": up, "down": down, "total": absorb + attn + up + down}
 
 
+def masked_flops(cfg, key_mask) -> dict:
+    """Absorbed-method FLOPs of one key-masked prefill call: query t of batch b
+    attends the visible keys s <= t only (masked keys are skipped)."""
+    B, T, H, d, r = cfg.B, cfg.T, cfg.H, cfg.d, cfg.r
+    visible = int(np.cumsum(key_mask.astype(np.int64), axis=1).sum())   # sum over (b, t) of visible keys s <= t
+    absorb = H * gemm_flops(B * T, d, r)
+    attn = 4 * H * r * visible
+    up = H * gemm_flops(B * T, r, d)
+    return {"absorb": absorb, "attn": attn, "up": up, "total": absorb + attn + up}
+
+
 def unabsorbed_flops(cfg) -> dict:
     """FLOPs of one prefill call in unabsorbed form: k and v materialised
     (2 B T r H d each), then causal attention at width d over t + 1 keys."""
@@ -126,7 +137,7 @@ def kernel_times(fn, steps: int):
     return {k: {"avg_ms": tot / n, "launches": n} for k, (tot, n) in stats.items()}
 
 
-def bench_prefill(cfg, steps, warmup, unabsorbed=False):
+def bench_prefill(cfg, steps, warmup, unabsorbed=False, masked=False):
     import torch
     import synth
     import rank_latent_causal_mla_amd as mla
@@ -135,12 +146,21 @@ def bench_prefill(cfg, steps, warmup, unabsorbed=False):
     dev = {k: to_device(v) for k, v in inp.items()}
     out = torch.empty_like(dev["q"])
     dt = mla.MLA_DTYPE_BF16 if cfg.dtype == "bf16" else mla.MLA_DTYPE_F32
-    size = mla.mla_latent_attn_unabsorbed_workspace_size if unabsorbed else mla.mla_latent_attn_workspace_size
+    if masked:
+        size = mla.mla_latent_attn_masked_workspace_size
+        inp["key_mask"] = synth.make_key_mask(cfg, p_hole=0.05)
+        kmask = torch.from_numpy(inp["key_mask"]).cuda()
+    else:
+        size = mla.mla_latent_attn_unabsorbed_workspace_size if unabsorbed else mla.mla_latent_attn_workspace_size
     fwd = mla.mla_latent_attn_fwd_unabsorbed if unabsorbed else mla.mla_latent_attn_fwd
     ws = torch.empty(size(cfg.B, cfg.T, cfg.H, cfg.d, cfg.r, dt), dtype=torch.uint8, device="cuda")
 
     def step(_i):
-        fwd(dev["q"], dev["kv_latent"], dev["w_up_k"], dev["w_up_v"], out=out, scale=cfg.scale, workspace=ws)
+        if masked:
+            mla.mla_latent_attn_fwd_masked(dev["q"], dev["kv_latent"], kmask, dev["w_up_k"], dev["w_up_v"], out=out,
+                                           scale=cfg.scale, workspace=ws)
+        else:
+            fwd(dev["q"], dev["kv_latent"], dev["w_up_k"], dev["w_up_v"], out=out, scale=cfg.scale, workspace=ws)
 
     ms = time_steps(step, steps, warmup)
     kt = kernel_times(step, steps)
@@ -230,6 +250,7 @@ def main(argv=None):
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-unabsorbed", action="store_true", help="skip the unabsorbed prefill timing")
+    ap.add_argument("--no-masked", action="store_true", help="skip the key-masked prefill timing")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (reference for HBM byte counters)")
     args = ap.parse_args(argv)
@@ -293,6 +314,18 @@ def main(argv=None):
             "value": round(uw["total"] / (ums * 1e-3) / 1e12, 2), "unit": "TFLOP/s", "ms_per_step": round(ums, 4),
             "flops_per_step": uw["total"], "step_time_vs_absorbed": round(ms / ums, 3), "roofline": uroof,
             "kernels_ms": {k: round(v["avg_ms"], 4) for k, v in ukt.items()}}
+    if not args.no_masked:
+        mms, mkt, minp = bench_prefill(cfg, args.steps, args.warmup, masked=True)
+        mw = masked_flops(cfg, minp["key_mask"])
+        mflash = mkt.get("flash_latent_bf16_masked")
+        line["masked"] = {
+            "what": "the same prefill with a key mask (mla_latent_attn_fwd_masked): per batch, keys past a valid "
+                    "length uniform on [T/2, T] and 5% of the rest masked; the visible keys are packed first and "
+                    "masked keys are skipped; value counts the visible causal keys only",
+            "value": round(mw["total"] / (mms * 1e-3) / 1e12, 2), "unit": "TFLOP/s",
+            "ms_per_step": round(mms, 4), "flops_per_step": mw["total"],
+            "flash_tflops": round(mw["attn"] / (mflash["avg_ms"] * 1e-3) / 1e12, 2) if mflash else None,
+            "kernels_ms": {k: round(v["avg_ms"], 4) for k, v in mkt.items()}}
     if not args.no_decode:
         dcfg = synth.CONFIGS[args.decode_workload]
         dms, dkt, lens = bench_decode(dcfg, max(args.steps, 10), args.warmup)

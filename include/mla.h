@@ -76,6 +76,25 @@ mla_status mla_latent_attn_fwd(const void* q, const void* kv_latent, const void*
                                int r, float scale, mla_dtype dt, void* workspace,
                                size_t workspace_bytes, void* stream);
 
+/* Bytes of workspace mla_latent_attn_fwd_masked needs for this shape (0 on bad sizes). */
+size_t mla_latent_attn_masked_workspace_size(int B, int T, int H, int d, int r, mla_dtype dt);
+
+/* Causal prefill with a key mask: mla_latent_attn_fwd where query t of batch
+ * b attends only the keys s <= t with key_mask[b,s] != 0.  A masked key's
+ * logit is -infinity before the softmax (the masked-score fill of
+ * POPCORNBENCH page Kimi-K2.6 l2_p29, its attention walk-through), so it
+ * gets weight 0; a query row with no visible key has an all -infinity row,
+ * whose softmax is undefined, and its output is NaN (what that page's
+ * analysis of fully masked rows finds such a softmax returns).
+ *   key_mask [B,T] uint8 in DEVICE memory (nonzero = visible), any alignment;
+ *   every other argument as mla_latent_attn_fwd.  workspace must hold
+ *   mla_latent_attn_masked_workspace_size() bytes.  With an all-nonzero mask
+ *   the result equals mla_latent_attn_fwd's bit for bit. */
+mla_status mla_latent_attn_fwd_masked(const void* q, const void* kv_latent, const uint8_t* key_mask,
+                                      const void* w_up_k, const void* w_up_v, void* out, int B, int T, int H,
+                                      int d, int r, float scale, mla_dtype dt, void* workspace,
+                                      size_t workspace_bytes, void* stream);
+
 /* Bytes of workspace mla_latent_attn_fwd_unabsorbed needs for this shape
  * (0 on bad sizes or a shape it does not cover). */
 size_t mla_latent_attn_unabsorbed_workspace_size(int B, int T, int H, int d, int r, mla_dtype dt);

@@ -19,6 +19,7 @@ MLA_OK, MLA_ERR_INVALID_ARGUMENT, MLA_ERR_UNSUPPORTED, MLA_ERR_WORKSPACE, MLA_ER
 MLA_DTYPE_F32, MLA_DTYPE_BF16 = 0, 1
 
 EXPORTED = ("mla_down_proj", "mla_latent_attn_workspace_size", "mla_latent_attn_fwd",
+            "mla_latent_attn_masked_workspace_size", "mla_latent_attn_fwd_masked",
             "mla_latent_attn_unabsorbed_workspace_size", "mla_latent_attn_fwd_unabsorbed",
             "mla_decode_workspace_size", "mla_decode_fwd", "mla_decode_varlen_workspace_size",
             "mla_decode_varlen_fwd", "mla_kv_append", "mla_profile_enable", "mla_profile_collect",
@@ -40,6 +41,15 @@ def load():
         return _lib
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is missing: build it with rank_latent_causal_mla_amd.build.build()")
+    # Let torch bring up the GPU runtime before the library's kernels are
+    # registered: loading the library first has left its own HIP calls
+    # without a visible device once torch initialised afterwards.
+    try:
+        import torch
+        if torch.cuda.is_available():
+            torch.cuda.init()
+    except ImportError:
+        pass
     lib = ctypes.CDLL(LIB_PATH)
     vp, i32, f32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
     lib.mla_down_proj.restype = i32
@@ -48,6 +58,11 @@ def load():
     lib.mla_latent_attn_workspace_size.argtypes = [i32] * 6
     lib.mla_latent_attn_fwd.restype = i32
     lib.mla_latent_attn_fwd.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, i32, vp, sz, vp]
+    lib.mla_latent_attn_masked_workspace_size.restype = sz
+    lib.mla_latent_attn_masked_workspace_size.argtypes = [i32] * 6
+    lib.mla_latent_attn_fwd_masked.restype = i32
+    lib.mla_latent_attn_fwd_masked.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, i32, vp, sz,
+                                               vp]
     lib.mla_latent_attn_unabsorbed_workspace_size.restype = sz
     lib.mla_latent_attn_unabsorbed_workspace_size.argtypes = [i32] * 6
     lib.mla_latent_attn_fwd_unabsorbed.restype = i32
@@ -98,6 +113,10 @@ def mla_latent_attn_workspace_size(B, T, H, d, r, dt):
     return int(load().mla_latent_attn_workspace_size(B, T, H, d, r, dt))
 
 
+def mla_latent_attn_masked_workspace_size(B, T, H, d, r, dt):
+    return int(load().mla_latent_attn_masked_workspace_size(B, T, H, d, r, dt))
+
+
 def mla_latent_attn_unabsorbed_workspace_size(B, T, H, d, r, dt):
     return int(load().mla_latent_attn_unabsorbed_workspace_size(B, T, H, d, r, dt))
 
@@ -109,6 +128,12 @@ def mla_decode_workspace_size(B, Tmax, H, d, r, dt):
 def mla_latent_attn_fwd_raw(q, kv_latent, w_up_k, w_up_v, out, B, T, H, d, r, scale, dt, ws, ws_bytes, stream=0):
     return load().mla_latent_attn_fwd(q, kv_latent, w_up_k, w_up_v, out, B, T, H, d, r, scale, dt, ws,
                                       ws_bytes, stream)
+
+
+def mla_latent_attn_fwd_masked_raw(q, kv_latent, key_mask, w_up_k, w_up_v, out, B, T, H, d, r, scale, dt, ws,
+                                   ws_bytes, stream=0):
+    return load().mla_latent_attn_fwd_masked(q, kv_latent, key_mask, w_up_k, w_up_v, out, B, T, H, d, r, scale, dt,
+                                             ws, ws_bytes, stream)
 
 
 def mla_latent_attn_fwd_unabsorbed_raw(q, kv_latent, w_up_k, w_up_v, out, B, T, H, d, r, scale, dt, ws, ws_bytes,
@@ -209,6 +234,36 @@ def mla_latent_attn_fwd(q, kv_latent, w_up_k, w_up_v, out=None, scale=None, work
     _check(mla_latent_attn_fwd_raw(q.data_ptr(), kv_latent.data_ptr(), w_up_k.data_ptr(), w_up_v.data_ptr(),
                                    out.data_ptr(), B, T, H, d, r, float(scale), dt, workspace.data_ptr(),
                                    workspace.numel() * workspace.element_size(), _stream(stream)))
+    return out
+
+
+def mla_latent_attn_fwd_masked(q, kv_latent, key_mask, w_up_k, w_up_v, out=None, scale=None, workspace=None,
+                               stream=None):
+    """Causal prefill with a key mask: key_mask[B,T] (uint8 or bool, device; nonzero = visible).
+    A query row with no visible key s <= t comes out NaN."""
+    import torch
+    _dev(q, kv_latent, key_mask, w_up_k, w_up_v)
+    B, T, H, d = q.shape
+    r = kv_latent.shape[-1]
+    if tuple(key_mask.shape) != (B, T):
+        raise ValueError("key_mask must be [B, T]")
+    if key_mask.dtype == torch.bool:
+        key_mask = key_mask.view(torch.uint8)
+    if key_mask.dtype != torch.uint8:
+        raise TypeError("key_mask must be uint8 or bool")
+    dt = _dt(q)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    nbytes = mla_latent_attn_masked_workspace_size(B, T, H, d, r, dt)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    _dev(out, workspace)
+    _check(mla_latent_attn_fwd_masked_raw(q.data_ptr(), kv_latent.data_ptr(), key_mask.data_ptr(), w_up_k.data_ptr(),
+                                          w_up_v.data_ptr(), out.data_ptr(), B, T, H, d, r, float(scale), dt,
+                                          workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                                          _stream(stream)))
     return out
 
 

@@ -422,10 +422,16 @@ struct Flash {
 // of tile j while the scores of tile j+1 run on the matrix unit, posts P_j,
 // then accumulates P_j L_j for its columns.  Tiles are copied three ahead;
 // blocks are issued heaviest (largest t) first.
-template <int R>
+// With COMPACT (key mask), lat holds each batch's visible keys packed in
+// order (zero rows after them) and cnt [B][T] the number of visible keys
+// s <= t: query t then attends packed keys 0 .. cnt[b][t] - 1, which are its
+// visible keys, through the same causal limit.  A row with no visible key
+// (cnt = 0) masks every key, ends with l = 0 and stores 0 / 0 = NaN, the
+// value the softmax of an all -infinity row takes.
+template <int R, bool COMPACT>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
 void flash_latent_bf16(const uint16_t* __restrict__ q_lat, const uint16_t* __restrict__ lat,
-                       uint16_t* __restrict__ o_lat, int B, int T, int H) {
+                       uint16_t* __restrict__ o_lat, int B, int T, int H, const int32_t* __restrict__ cnt) {
   using F = Flash<R>;
   constexpr int TILE = kTileKeys * R * 2;
   constexpr int NI = TILE / 1024 / 4;  // copy instructions per wave and tile
@@ -434,6 +440,10 @@ void flash_latent_bf16(const uint16_t* __restrict__ q_lat, const uint16_t* __res
   char* pbuf = smem + kFlashBufs * TILE;         // [8 q][64 lanes] x 16 bytes of P
   float* abuf = (float*)(pbuf + F::NQ * 1024);   // [8 q][16] rescale factors, then l
   int* fbuf = (int*)(abuf + F::NQ * 16);         // [4]: wave w's rows rescale this tile
+  // COMPACT: [4 w][2 qb][64 lanes] last key of each row, read back per tile
+  // by the lane that wrote it (a loaded value kept in a register would be
+  // spilled, and a scratch reload inside the loop waits on the tile copies)
+  int* tbuf = fbuf + 4;
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int G = lane >> 4, n = lane & 15;
@@ -443,20 +453,26 @@ void flash_latent_bf16(const uint16_t* __restrict__ q_lat, const uint16_t* __res
   const int b = blockIdx.x % B;
   const long row0 = (long)rb * 128;
   const long row_end = TH < row0 + 128 ? TH : row0 + 128;
-  const int t_last_blk = (int)((row_end - 1) / H);
-  const int ntiles = t_last_blk / kTileKeys + 1;
+  // last key position row t attends (cnt is nondecreasing in t)
+  auto last_key = [&](int t) { return COMPACT ? cnt[(size_t)b * T + t] - 1 : t; };
+  const int t_last_blk = last_key((int)((row_end - 1) / H));
+  const int ntiles = t_last_blk / kTileKeys + 1;  // at least 1 (-1 / 32 = 0)
   // rows owned for the scores: 32 w .. 32 w + 31 of the block
   const long wrow0 = row0 + 32 * w;
-  const int t_first_w = (int)((wrow0 < TH ? wrow0 : TH - 1) / H);
+  const int t_first_w = last_key((int)((wrow0 < TH ? wrow0 : TH - 1) / H));
   long my_row[2];
   int t_row[2];
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
     my_row[qb] = wrow0 + 16 * qb + n;
-    t_row[qb] = (int)((my_row[qb] < TH ? my_row[qb] : TH - 1) / H);
+    t_row[qb] = last_key((int)((my_row[qb] < TH ? my_row[qb] : TH - 1) / H));
   }
   const uint16_t* latb = lat + (size_t)b * T * R;
   const uint32_t lds0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)smem);
+  if (COMPACT) {
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) tbuf[(2 * w + qb) * 64 + lane] = t_row[qb];
+  }
 
   // first tiles in flight while the queries load
 #pragma unroll
@@ -499,7 +515,9 @@ void flash_latent_bf16(const uint16_t* __restrict__ q_lat, const uint16_t* __res
     const int k0 = kTileKeys * j;
     int lim[2];
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) lim[qb] = t_row[qb] - k0 - 4 * G;
+    for (int qb = 0; qb < 2; ++qb)
+      lim[qb] = (COMPACT ? *(const __attribute__((address_space(3))) int*)(uintptr_t)(tbuf + (2 * w + qb) * 64 + lane)
+                         : t_row[qb]) - k0 - 4 * G;
     bf16x8 P[2];
     float alpha[2];
     // scores of tile j + 1 (after the last tile: a stale buffer, discarded)
@@ -550,7 +568,8 @@ void flash_latent_bf16(const uint16_t* __restrict__ q_lat, const uint16_t* __res
     }
     // refill the buffer of tile j - 1 (every wave is past it) while the matrix ops run
     if (j + kFlashBufs - 1 < ntiles)
-      dma_tile32<R>(latb, kTileKeys * (j + kFlashBufs - 1), T, lds0 + ((j + kFlashBufs - 1) % kFlashBufs) * TILE, w);
+      dma_tile32<R, COMPACT>(latb, kTileKeys * (j + kFlashBufs - 1), T,
+                             lds0 + ((j + kFlashBufs - 1) % kFlashBufs) * TILE, w);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -589,16 +608,72 @@ void flash_latent_bf16(const uint16_t* __restrict__ q_lat, const uint16_t* __res
 }
 
 // ---------------------------------------------------------------------------
+// Key mask -> packed keys.  compact_scan: one block of 1024 per batch walks
+// key_mask[b] [T] bytes (nonzero = visible) in chunks of 1024 and writes
+// cnt[b][t] = number of visible keys s <= t and src[b][j] = the position of
+// the j-th visible key.  compact_gather: one wave per packed row j copies
+// latent row src[b][j] of batch b (or zeros for j >= cnt[b][T - 1]).
+__global__ __launch_bounds__(1024) void compact_scan(const uint8_t* __restrict__ key_mask,
+                                                     int32_t* __restrict__ cnt, int32_t* __restrict__ src, int T) {
+  __shared__ int wsum[16];
+  const int b = blockIdx.x;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const uint8_t* m = key_mask + (size_t)b * T;
+  int32_t* cb = cnt + (size_t)b * T;
+  int32_t* sb = src + (size_t)b * T;
+  int run = 0;  // visible keys before this chunk (block-uniform)
+  for (int c0 = 0; c0 < T; c0 += 1024) {
+    const int t = c0 + threadIdx.x;
+    const bool vis = t < T && m[t] != 0;
+    const uint64_t bal = __builtin_amdgcn_ballot_w64(vis);
+    const int below = __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0));
+    if (lane == 0) wsum[w] = __builtin_popcountll(bal);
+    __syncthreads();
+    int before = run;
+    for (int i = 0; i < w; ++i) before += wsum[i];
+    int total = 0;
+    for (int i = 0; i < 16; ++i) total += wsum[i];
+    if (t < T) {
+      const int k = before + below;  // visible keys before t
+      cb[t] = k + (vis ? 1 : 0);
+      if (vis) sb[k] = t;
+    }
+    run += total;
+    __syncthreads();  // wsum is rewritten by the next chunk
+  }
+}
+
+template <int R>
+__global__ __launch_bounds__(256) void compact_gather(const uint16_t* __restrict__ lat, const int32_t* __restrict__ cnt,
+                                                      const int32_t* __restrict__ src, uint16_t* __restrict__ lat_c,
+                                                      int T) {
+  static_assert(R % 8 == 0 && R / 8 <= 64, "one 16-byte chunk per lane");
+  const int b = blockIdx.y;
+  const int j = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (j >= T || lane >= R / 8) return;
+  const int nvis = cnt[(size_t)b * T + T - 1];
+  u32x4 v = {0u, 0u, 0u, 0u};
+  if (j < nvis) v = *(const u32x4*)(lat + ((size_t)b * T + src[(size_t)b * T + j]) * R + 8 * lane);
+  *(u32x4*)(lat_c + ((size_t)b * T + j) * R + 8 * lane) = v;
+}
+
+// ---------------------------------------------------------------------------
 // Host-side launchers (called by the C ABI after validation).
 template <int R>
 static hipError_t run_prefill(const uint16_t* q, const uint16_t* lat, const uint16_t* wk,
                               const uint16_t* wv, uint16_t* out, int B, int T, int H, int d,
-                              float sl2, uint16_t* q_lat, uint16_t* o_lat, uint16_t* wvT, hipStream_t st) {
+                              float sl2, uint16_t* q_lat, uint16_t* o_lat, uint16_t* wvT,
+                              const uint8_t* key_mask, int32_t* cnt, int32_t* src, uint16_t* lat_c,
+                              hipStream_t st) {
   const int N = B * T;
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)flash_latent_bf16<R>,
+    hipError_t e = hipFuncSetAttribute((const void*)flash_latent_bf16<R, false>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)flash_lds_bytes(R));
+    if (e == hipSuccess)
+      e = hipFuncSetAttribute((const void*)flash_latent_bf16<R, true>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)flash_lds_bytes(R));
     if (e == hipSuccess)
       e = hipFuncSetAttribute((const void*)up_bf16<R, false>, hipFuncAttributeMaxDynamicSharedMemorySize,
                               (int)up_lds_bytes<R>());
@@ -614,10 +689,19 @@ static hipError_t run_prefill(const uint16_t* q, const uint16_t* lat, const uint
   }
   const long TH = (long)T * H;
   const int nrb = (int)((TH + 127) / 128);
-  {
+  if (key_mask) {
+    {
+      ProfScope ps("compact_keys", st);
+      hipLaunchKernelGGL(compact_scan, dim3(B), dim3(1024), 0, st, key_mask, cnt, src, T);
+      hipLaunchKernelGGL(compact_gather<R>, dim3((T + 3) / 4, B), dim3(256), 0, st, lat, cnt, src, lat_c, T);
+    }
+    ProfScope ps("flash_latent_bf16_masked", st);
+    hipLaunchKernelGGL((flash_latent_bf16<R, true>), dim3(B * nrb), dim3(256), flash_lds_bytes(R), st, q_lat, lat_c,
+                       o_lat, B, T, H, (const int32_t*)cnt);
+  } else {
     ProfScope ps("flash_latent_bf16", st);
-    hipLaunchKernelGGL(flash_latent_bf16<R>, dim3(B * nrb), dim3(256), flash_lds_bytes(R), st, q_lat, lat, o_lat,
-                       B, T, H);
+    hipLaunchKernelGGL((flash_latent_bf16<R, false>), dim3(B * nrb), dim3(256), flash_lds_bytes(R), st, q_lat, lat,
+                       o_lat, B, T, H, (const int32_t*)nullptr);
   }
   {
     ProfScope ps("up_bf16", st);
@@ -627,15 +711,21 @@ static hipError_t run_prefill(const uint16_t* q, const uint16_t* lat, const uint
   return hipGetLastError();
 }
 
-// Workspace: q_lat [B*T*H][r] | o_lat [B*T*H][r] | W_uv^T [H][d][r], all bf16.
+// Workspace: q_lat [B*T*H][r] | o_lat [B*T*H][r] | W_uv^T [H][d][r], all bf16;
+// with a key mask, then (at a 256-byte boundary) the packed latents
+// [B][T][r] bf16 | cnt [B][T] int32 | src [B][T] int32.
 hipError_t prefill_mfma(const void* q, const void* lat, const void* wk, const void* wv, void* out,
-                        int B, int T, int H, int d, int r, float sl2, void* ws, hipStream_t st) {
+                        int B, int T, int H, int d, int r, float sl2, const uint8_t* key_mask, void* ws,
+                        hipStream_t st) {
   const size_t rows = (size_t)B * T * H;
   uint16_t* q_lat = (uint16_t*)ws;
   uint16_t* o_lat = q_lat + rows * r;
   uint16_t* wvT = o_lat + rows * r;
+  uint16_t* lat_c = (uint16_t*)((char*)ws + prefill_mfma_workspace(B, T, H, d, r));
+  int32_t* cnt = (int32_t*)(lat_c + (size_t)B * T * r);
+  int32_t* src = cnt + (size_t)B * T;
 #define ARGS (const uint16_t*)q, (const uint16_t*)lat, (const uint16_t*)wk, (const uint16_t*)wv, \
-             (uint16_t*)out, B, T, H, d, sl2, q_lat, o_lat, wvT, st
+             (uint16_t*)out, B, T, H, d, sl2, q_lat, o_lat, wvT, key_mask, cnt, src, lat_c, st
   switch (r) {
     case 128: return run_prefill<128>(ARGS);
     case 256: return run_prefill<256>(ARGS);
@@ -687,7 +777,9 @@ hipError_t materialise_kv(const uint16_t* lat, const uint16_t* wk, const uint16_
 
 size_t prefill_mfma_workspace(int B, int T, int H, int d, int r) {
   const size_t rows = (size_t)B * T * H;
-  return (2 * rows * r + (size_t)H * d * r) * 2;
+  return ((2 * rows * r + (size_t)H * d * r) * 2 + 255) / 256 * 256;
 }
+
+size_t key_mask_workspace(int B, int T, int r) { return (size_t)B * T * (8 + 2 * (size_t)r); }
 
 }  // namespace mla

@@ -39,14 +39,17 @@ __global__ void absorb_simt(const T* __restrict__ q, const T* __restrict__ wk,
 }
 
 // Streaming-softmax attention of one query row per wave over the latents.
-// Prefill: row = (b*T + t)*H + h attends keys 0..t of batch b.
+// Prefill: row = (b*T + t)*H + h attends keys 0..t of batch b; with kmask
+//          [B, T] bytes, only the keys s whose kmask[b, s] is nonzero (a masked
+//          logit is -infinity; a row with no visible key gives 0 / 0 = NaN).
 // Decode:  row = b*H + h attends keys 0..L_b-1 (L_b = seq_lens[b] clamped to [1, Tl]) of a
 //          padded cache [B, Tl, R]; with cu, the rows cu[b] .. cu[b+1]-1 of a packed cache
 //          [Tl, R] (clamped into the cache, as the matrix-core path does).
 template <typename T, bool DECODE>
 __global__ void attend_simt(const float* __restrict__ q_lat, const T* __restrict__ lat,
                             const int32_t* __restrict__ lens, const int32_t* __restrict__ cu,
-                            float* __restrict__ o_lat, int Tl, int H, int R, float sl2, long nrows) {
+                            const uint8_t* __restrict__ kmask, float* __restrict__ o_lat, int Tl, int H,
+                            int R, float sl2, long nrows) {
   __shared__ float qs[4][1024];
   __shared__ float ps[4][64];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -82,15 +85,17 @@ __global__ void attend_simt(const float* __restrict__ q_lat, const T* __restrict
   for (int s0 = 0; s0 < nkeys; s0 += 64) {
     const int s = s0 + lane;
     float x = -INFINITY;
-    if (s < nkeys) {
+    if (s < nkeys && (DECODE || !kmask || kmask[base + s])) {
       const T* lr = latb + (size_t)s * R;
       float dot = 0.f;
       for (int rho = 0; rho < R; ++rho) dot += qs[w][rho] * io<T>::ld(lr, rho);
       x = dot * sl2;
     }
-    const float mn = fmaxf(m, wave_max(x));  // finite: key s0 is always valid
-    const float alpha = exp2f(m - mn);
-    const float p = exp2f(x - mn);
+    const float mn = fmaxf(m, wave_max(x));
+    // no visible key yet: mn = -inf, subtract 0 so the weights are exact zeros
+    const float msub = mn == -INFINITY ? 0.f : mn;
+    const float alpha = exp2f(m - msub);
+    const float p = exp2f(x - msub);
     l = l * alpha + wave_sum(p);
     m = mn;
     ps[w][lane] = p;
@@ -175,7 +180,8 @@ __global__ void gemm_simt(const T* __restrict__ A, const T* __restrict__ Bm, T* 
 
 template <typename T>
 static hipError_t prefill_simt_t(const T* q, const T* lat, const T* wk, const T* wv, T* out, int B,
-                                 int T_, int H, int d, int r, float sl2, void* ws, hipStream_t st) {
+                                 int T_, int H, int d, int r, float sl2, const uint8_t* kmask, void* ws,
+                                 hipStream_t st) {
   const long rows = (long)B * T_ * H;
   float* q_lat = (float*)ws;
   float* o_lat = q_lat + (size_t)rows * r;
@@ -186,7 +192,7 @@ static hipError_t prefill_simt_t(const T* q, const T* lat, const T* wk, const T*
   {
     ProfScope ps("attend_simt", st);
     hipLaunchKernelGGL((attend_simt<T, false>), dim3((rows + 3) / 4), dim3(256), 0, st, q_lat, lat, nullptr,
-                       (const int32_t*)nullptr, o_lat, T_, H, r, sl2, rows);
+                       (const int32_t*)nullptr, kmask, o_lat, T_, H, r, sl2, rows);
   }
   {
     ProfScope ps("up_simt", st);
@@ -209,7 +215,7 @@ static hipError_t decode_simt_t(const T* q, const T* lat, const int32_t* lens, c
   {
     ProfScope ps("attend_simt", st);
     hipLaunchKernelGGL((attend_simt<T, true>), dim3((rows + 3) / 4), dim3(256), 0, st, q_lat, lat,
-                       lens, cu, o_lat, Tmax, H, r, sl2, rows);
+                       lens, cu, (const uint8_t*)nullptr, o_lat, Tmax, H, r, sl2, rows);
   }
   {
     ProfScope ps("up_simt", st);
@@ -221,14 +227,14 @@ static hipError_t decode_simt_t(const T* q, const T* lat, const int32_t* lens, c
 static constexpr float kLog2e = 1.4426950408889634f;
 
 hipError_t prefill_simt(bool bf16, const void* q, const void* lat, const void* wk, const void* wv,
-                        void* out, int B, int T, int H, int d, int r, float scale, void* ws,
-                        hipStream_t st) {
+                        void* out, int B, int T, int H, int d, int r, float scale, const uint8_t* key_mask,
+                        void* ws, hipStream_t st) {
   const float sl2 = scale * kLog2e;
   if (bf16)
     return prefill_simt_t((const uint16_t*)q, (const uint16_t*)lat, (const uint16_t*)wk,
-                          (const uint16_t*)wv, (uint16_t*)out, B, T, H, d, r, sl2, ws, st);
+                          (const uint16_t*)wv, (uint16_t*)out, B, T, H, d, r, sl2, key_mask, ws, st);
   return prefill_simt_t((const float*)q, (const float*)lat, (const float*)wk, (const float*)wv,
-                        (float*)out, B, T, H, d, r, sl2, ws, st);
+                        (float*)out, B, T, H, d, r, sl2, key_mask, ws, st);
 }
 
 size_t prefill_simt_workspace(int B, int T, int H, int d, int r) {

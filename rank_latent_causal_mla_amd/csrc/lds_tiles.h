@@ -64,13 +64,18 @@ __device__ __forceinline__ int tswz(int key) { return ((key & 3) << 1) | ((key >
 // of the tile's 32 R * 2 / 1024, each 64 lanes x 16 bytes.  The swizzle is
 // applied on the global side: LDS-DMA writes lane l to byte 16 l of its
 // 1 KB destination, so lane l fetches the chunk that belongs there.
-template <int R>
+// With REMAT the per-lane offsets are recomputed at every call instead of
+// being kept as loop invariants (eight registers at R = 512), for kernels
+// that are out of registers: a spilled offset is reloaded from scratch with
+// a wait for every copy in flight.
+template <int R, bool REMAT = false>
 __device__ __forceinline__ void dma_tile32(const uint16_t* latb, int k0, int kend, uint32_t tile, int w) {
   constexpr int NC = R / 8;    // 16-byte chunks per key row
   constexpr int RPI = 64 / NC;  // key rows per instruction
   constexpr int NI = kTileKeys * R * 2 / 1024 / 4;  // instructions per wave
   static_assert(NC <= 64 && 64 % NC == 0, "a copy instruction covers whole rows");
-  const int lane = threadIdx.x & 63;
+  int lane = threadIdx.x & 63;
+  if (REMAT) asm volatile("" : "+v"(lane));
   const int sl = lane / NC, p = lane % NC;
 #pragma unroll
   for (int i = 0; i < NI; ++i) {

@@ -104,10 +104,20 @@ size_t mla_latent_attn_workspace_size(int B, int T, int H, int d, int r, mla_dty
                             : mla::prefill_simt_workspace(B, T, H, d, r);
 }
 
-mla_status mla_latent_attn_fwd(const void* q, const void* kv_latent, const void* w_up_k,
-                               const void* w_up_v, void* out, int B, int T, int H, int d, int r,
-                               float scale, mla_dtype dt, void* workspace, size_t workspace_bytes,
-                               void* stream) {
+size_t mla_latent_attn_masked_workspace_size(int B, int T, int H, int d, int r, mla_dtype dt) {
+  const size_t base = mla_latent_attn_workspace_size(B, T, H, d, r, dt);
+  if (base == 0) return 0;
+  return use_mfma(dt, d, r) ? base + mla::key_mask_workspace(B, T, r) : base;
+}
+
+}  // extern "C"
+
+namespace {
+
+// Prefill with (key_mask) or without a key mask.
+mla_status prefill_common(const void* q, const void* kv_latent, const uint8_t* key_mask, const void* w_up_k,
+                          const void* w_up_v, void* out, int B, int T, int H, int d, int r, float scale,
+                          mla_dtype dt, void* workspace, size_t workspace_bytes, void* stream) {
   if (!q || !kv_latent || !w_up_k || !w_up_v || !out || !workspace)
     return fail(MLA_ERR_INVALID_ARGUMENT, "null pointer");
   mla_status s = check_dims(B, T, H, d, r, dt, "T");
@@ -116,7 +126,8 @@ mla_status mla_latent_attn_fwd(const void* q, const void* kv_latent, const void*
   if (!aligned16(q) || !aligned16(kv_latent) || !aligned16(w_up_k) || !aligned16(w_up_v) ||
       !aligned16(out) || !aligned16(workspace))
     return fail(MLA_ERR_INVALID_ARGUMENT, "pointers must be 16-byte aligned");
-  const size_t need = mla_latent_attn_workspace_size(B, T, H, d, r, dt);
+  const size_t need = key_mask ? mla_latent_attn_masked_workspace_size(B, T, H, d, r, dt)
+                               : mla_latent_attn_workspace_size(B, T, H, d, r, dt);
   if (workspace_bytes < need)
     return fail(MLA_ERR_WORKSPACE, "workspace %zu bytes < %zu required", workspace_bytes, need);
   hipStream_t st = (hipStream_t)stream;
@@ -130,11 +141,32 @@ mla_status mla_latent_attn_fwd(const void* q, const void* kv_latent, const void*
   }
   if (use_mfma(dt, d, r))
     return launched(mla::prefill_mfma(q, kv_latent, w_up_k, w_up_v, out, B, T, H, d, r,
-                                      (float)(scale * kLog2e), workspace, st),
+                                      (float)(scale * kLog2e), key_mask, workspace, st),
                     "prefill launch");
   return launched(mla::prefill_simt(dt == MLA_DTYPE_BF16, q, kv_latent, w_up_k, w_up_v, out, B, T,
-                                    H, d, r, scale, workspace, st),
+                                    H, d, r, scale, key_mask, workspace, st),
                   "prefill launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+mla_status mla_latent_attn_fwd(const void* q, const void* kv_latent, const void* w_up_k,
+                               const void* w_up_v, void* out, int B, int T, int H, int d, int r,
+                               float scale, mla_dtype dt, void* workspace, size_t workspace_bytes,
+                               void* stream) {
+  return prefill_common(q, kv_latent, nullptr, w_up_k, w_up_v, out, B, T, H, d, r, scale, dt, workspace,
+                        workspace_bytes, stream);
+}
+
+mla_status mla_latent_attn_fwd_masked(const void* q, const void* kv_latent, const uint8_t* key_mask,
+                                      const void* w_up_k, const void* w_up_v, void* out, int B, int T, int H,
+                                      int d, int r, float scale, mla_dtype dt, void* workspace,
+                                      size_t workspace_bytes, void* stream) {
+  if (!key_mask) return fail(MLA_ERR_INVALID_ARGUMENT, "null pointer");
+  return prefill_common(q, kv_latent, key_mask, w_up_k, w_up_v, out, B, T, H, d, r, scale, dt, workspace,
+                        workspace_bytes, stream);
 }
 
 size_t mla_latent_attn_unabsorbed_workspace_size(int B, int T, int H, int d, int r, mla_dtype dt) {

@@ -17,14 +17,20 @@ size_t decode_max_splits(int B);
 constexpr size_t decode_lds_bytes(int R) { return (size_t)4 * 32 * R * 2 + 2048 + 512; }
 
 // LDS of the prefill flash kernel: a ring of four 32-key latent tiles, one
-// tile's probabilities for 128 rows (8 KB), 128 rescale factors and 4 flags.
-constexpr size_t flash_lds_bytes(int R) { return (size_t)4 * 32 * R * 2 + 8 * 1024 + 8 * 16 * 4 + 16; }
+// tile's probabilities for 128 rows (8 KB), 128 rescale factors, 4 flags and
+// (key-masked form) the last visible key of the 512 (row, lane) slots.
+constexpr size_t flash_lds_bytes(int R) { return (size_t)4 * 32 * R * 2 + 8 * 1024 + 8 * 16 * 4 + 16 + 2048; }
 
 // ---- bf16 matrix-core path (r in {128, 256, 512}, d in {32, 64, 128, 256})
 bool mfma_supported(int d, int r);
+// key_mask [B][T] bytes (nonzero = visible) or null; with it the workspace holds
+// prefill_mfma_workspace() + key_mask_workspace() bytes (the visible keys are
+// packed there before the attention).
 hipError_t prefill_mfma(const void* q, const void* lat, const void* wk, const void* wv, void* out,
-                        int B, int T, int H, int d, int r, float sl2, void* ws, hipStream_t st);
+                        int B, int T, int H, int d, int r, float sl2, const uint8_t* key_mask, void* ws,
+                        hipStream_t st);
 size_t prefill_mfma_workspace(int B, int T, int H, int d, int r);
+size_t key_mask_workspace(int B, int T, int r);
 size_t decode_mfma_workspace(int B, int Tmax, int H, int d, int r);
 // lens (padded cache [B, Tmax, r]) or cu (packed cache [Tmax = total rows, r]; lens unused)
 hipError_t decode_mfma(const void* q, const void* lat, const int32_t* lens, const int32_t* cu, const void* wk,
@@ -49,9 +55,10 @@ hipError_t materialise_kv(const uint16_t* lat, const uint16_t* wk, const uint16_
 
 // ---- SIMT path: float32 (or bf16 storage) with float32 arithmetic, any r <= 1024, d <= 256
 // dt_bf16: inputs and outputs stored as bf16 (else float32).
+// key_mask [B][T] bytes (nonzero = visible) or null.
 hipError_t prefill_simt(bool dt_bf16, const void* q, const void* lat, const void* wk,
                         const void* wv, void* out, int B, int T, int H, int d, int r,
-                        float scale, void* ws, hipStream_t st);
+                        float scale, const uint8_t* key_mask, void* ws, hipStream_t st);
 size_t prefill_simt_workspace(int B, int T, int H, int d, int r);
 hipError_t decode_simt(bool dt_bf16, const void* q, const void* lat, const int32_t* lens, const int32_t* cu,
                        const void* wk, const void* wv, void* out, int B, int Tmax, int H, int d,

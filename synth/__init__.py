@@ -31,7 +31,8 @@ import subprocess
 
 import numpy as np
 
-from .configs import CONFIGS, TENSOR_IDS, WORKLOADS, Config, make_inputs, make_rows, seq_lens  # noqa: F401
+from .configs import (CONFIGS, TENSOR_IDS, WORKLOADS, Config, make_inputs, make_key_mask, make_rows,  # noqa: F401
+                      seq_lens)
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SO = os.path.join(_HERE, "libsynth.so")

@@ -14,7 +14,8 @@ import math
 import numpy as np
 
 # stream ids: one independent stream per tensor role
-TENSOR_IDS = {"q": 1, "kv_latent": 2, "w_up_k": 3, "w_up_v": 4, "hidden": 5, "w_down": 6, "seq_lens": 7}
+TENSOR_IDS = {"q": 1, "kv_latent": 2, "w_up_k": 3, "w_up_v": 4, "hidden": 5, "w_down": 6, "seq_lens": 7,
+              "key_mask": 8, "key_valid_len": 9}
 SEED_BASE = 0x4D4C41
 
 
@@ -108,3 +109,20 @@ def make_rows(cfg: Config, name: str, b: int, t0: int, nrows: int) -> np.ndarray
         raise ValueError(name)
     start = (b * T + t0) * row
     return normal_tensor(cfg.seed, TENSOR_IDS[name], (nrows, row), std, cfg.dtype, start=start)
+
+
+def make_key_mask(cfg: Config, p_hole: float = 0.1, pad: bool = True, lead: int = 0) -> np.ndarray:
+    """A key mask [B, T] uint8 (1 = visible) in the shape of padded batches:
+    with `pad`, batch b keeps keys below a valid length uniform on [T/2, T]
+    (both ends included) and masks the rest; every key is also masked with
+    probability p_hole (independent uniforms); the first `lead` keys of odd
+    batches are masked, so their first rows see no key at all."""
+    from . import randint, uniform
+    B, T = cfg.B, cfg.T
+    u = uniform(cfg.seed, TENSOR_IDS["key_mask"], 0, B * T).reshape(B, T)
+    mask = (u >= p_hole).astype(np.uint8)
+    if pad:
+        valid = randint(cfg.seed, TENSOR_IDS["key_valid_len"], B, (T + 1) // 2, T)
+        mask[np.arange(T)[None, :] >= valid[:, None]] = 0
+    mask[1::2, :lead] = 0
+    return mask

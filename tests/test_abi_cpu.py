@@ -169,3 +169,44 @@ def test_workspace_sizes():
     assert mla.mla_latent_attn_workspace_size(0, 1, 1, 1, 1, F32) == 0
     assert mla.mla_decode_workspace_size(64, 8192, 32, 128, 512, BF16) > 64 * 32 * 512 * 4
     assert mla.mla_decode_workspace_size(1, 1, 1, 1, 1, 9) == 0
+
+
+def masked(**kw):
+    a = dict(q=P, kv=P, mask=P + 1, wk=P, wv=P, out=P, B=2, T=64, H=4, d=32, r=32, scale=0.17, dt=F32, ws=P,
+             wsb=1 << 40)
+    a.update(kw)
+    return mla.mla_latent_attn_fwd_masked_raw(a["q"], a["kv"], a["mask"], a["wk"], a["wv"], a["out"], a["B"], a["T"],
+                                              a["H"], a["d"], a["r"], a["scale"], a["dt"], a["ws"], a["wsb"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    ({"mask": 0}, mla.MLA_ERR_INVALID_ARGUMENT),
+    ({"q": 0}, mla.MLA_ERR_INVALID_ARGUMENT),
+    ({"T": 0}, mla.MLA_ERR_INVALID_ARGUMENT),
+    ({"dt": 4}, mla.MLA_ERR_INVALID_ARGUMENT),
+    ({"scale": float("nan")}, mla.MLA_ERR_INVALID_ARGUMENT),
+    ({"kv": P + 4}, mla.MLA_ERR_INVALID_ARGUMENT),
+    ({"r": 2048}, mla.MLA_ERR_UNSUPPORTED),
+    ({"wsb": 1000}, mla.MLA_ERR_WORKSPACE),
+])
+def test_masked_argument_errors(kw, status):
+    assert masked(**kw) == status
+    assert mla.last_error() != ""
+
+
+def test_masked_needs_room_for_the_mask_bits():
+    # bf16 matrix-core shape: the unmasked workspace is too small (the mask bits follow it)
+    wsb = mla.mla_latent_attn_workspace_size(2, 100, 4, 128, 512, BF16)
+    assert masked(dt=BF16, d=128, r=512, T=100, wsb=wsb) == mla.MLA_ERR_WORKSPACE
+
+
+def test_masked_workspace_size():
+    # bf16 matrix-core path: the unmasked workspace, then the packed visible latents [B][T][r] bf16 and
+    # two int32 tables [B][T] (visible keys up to t, position of the j-th visible key)
+    for T in (1, 32, 33, 100, 16384):
+        assert mla.mla_latent_attn_masked_workspace_size(2, T, 4, 128, 512, BF16) == \
+            mla.mla_latent_attn_workspace_size(2, T, 4, 128, 512, BF16) + 2 * T * (512 * 2 + 8)
+    # float32 path reads the byte mask directly
+    assert mla.mla_latent_attn_masked_workspace_size(2, 64, 4, 32, 32, F32) == \
+        mla.mla_latent_attn_workspace_size(2, 64, 4, 32, 32, F32)
+    assert mla.mla_latent_attn_masked_workspace_size(0, 64, 4, 32, 32, F32) == 0

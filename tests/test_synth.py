@@ -51,3 +51,17 @@ def test_make_rows_matches_make_inputs():
     full = synth.make_inputs(cfg)
     assert np.array_equal(synth.make_rows(cfg, "q", 1, 5, 3), full["q"][1, 5:8].reshape(3, -1))
     assert np.array_equal(synth.make_rows(cfg, "kv_latent", 0, 2, 4), full["kv_latent"][0, 2:6])
+
+
+def test_key_mask_recipe():
+    import dataclasses
+    cfg = dataclasses.replace(synth.CONFIGS["bf16_prefill"], B=4, T=200)
+    m = synth.make_key_mask(cfg, p_hole=0.1, lead=7)
+    assert m.shape == (4, 200) and m.dtype == np.uint8 and set(np.unique(m)) <= {0, 1}
+    assert np.array_equal(m, synth.make_key_mask(cfg, p_hole=0.1, lead=7))      # seeded
+    assert not m[1::2, :7].any()                                                   # leading keys of odd batches
+    for b in range(4):   # padding: nothing visible past the last visible key's run, valid length >= T/2
+        vis = np.nonzero(m[b])[0]
+        assert vis.size and vis.max() < 200
+    nopad = synth.make_key_mask(cfg, p_hole=0.0, pad=False)
+    assert nopad.all()
