@@ -167,6 +167,28 @@ def bench_prefill(cfg, steps, warmup, unabsorbed=False, masked=False):
     return ms, kt, inp
 
 
+def bench_full(cfg, steps, warmup):
+    """The full path in one call (mla_latent_attn_fwd_full): down-projection into the latent cache, then the
+    causal prefill."""
+    import torch
+    import synth
+    import rank_latent_causal_mla_amd as mla
+    from tests.helpers import to_device
+    inp = synth.make_inputs(cfg)
+    dev = {k: to_device(v) for k, v in inp.items()}
+    out = torch.empty_like(dev["q"])
+    lat = torch.empty((cfg.B, cfg.T, cfg.r), dtype=dev["q"].dtype, device="cuda")
+    dt = mla.MLA_DTYPE_BF16 if cfg.dtype == "bf16" else mla.MLA_DTYPE_F32
+    ws = torch.empty(mla.mla_latent_attn_full_workspace_size(cfg.B, cfg.T, cfg.D, cfg.H, cfg.d, cfg.r, dt),
+                     dtype=torch.uint8, device="cuda")
+
+    def step(_i):
+        mla.mla_latent_attn_fwd_full(dev["hidden"], dev["w_down"], dev["q"], dev["w_up_k"], dev["w_up_v"],
+                                     kv_latent=lat, out=out, scale=cfg.scale, workspace=ws)
+
+    return time_steps(step, steps, warmup), kernel_times(step, steps)
+
+
 def bench_decode_varlen(cfg, steps, warmup, copies=3):
     """The same decode over packed caches [sum L, r] with cu_seqlens (rotated copies as above)."""
     import torch
@@ -251,6 +273,7 @@ def main(argv=None):
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-unabsorbed", action="store_true", help="skip the unabsorbed prefill timing")
     ap.add_argument("--no-masked", action="store_true", help="skip the key-masked prefill timing")
+    ap.add_argument("--no-full", action="store_true", help="skip the full-path (down-projection + prefill) timing")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (reference for HBM byte counters)")
     args = ap.parse_args(argv)
@@ -326,6 +349,23 @@ def main(argv=None):
             "ms_per_step": round(mms, 4), "flops_per_step": mw["total"],
             "flash_tflops": round(mw["attn"] / (mflash["avg_ms"] * 1e-3) / 1e12, 2) if mflash else None,
             "kernels_ms": {k: round(v["avg_ms"], 4) for k, v in mkt.items()}}
+    if not args.no_full:
+        import dataclasses
+        line["full_path"] = []
+        for fcfg in (synth.CONFIGS["fp32_full_path"],
+                     dataclasses.replace(synth.CONFIGS["bf16_prefill"], name="bf16_prefill_down1024", D=1024)):
+            fms, fkt = bench_full(fcfg, args.steps, args.warmup)
+            fw = prefill_flops(fcfg)
+            down = fkt.get("down_bf16") or fkt.get("gemm_simt")
+            line["full_path"].append({
+                "what": "mla_latent_attn_fwd_full: kv_latent = hidden @ w_down written as the latent cache, then the "
+                        "causal prefill; value counts the down-projection and the absorbed-method FLOPs",
+                "workload": fcfg.name, "dtype": fcfg.dtype,
+                "shape": {"B": fcfg.B, "T": fcfg.T, "D": fcfg.D, "H": fcfg.H, "d": fcfg.d, "r": fcfg.r},
+                "value": round(fw["total"] / (fms * 1e-3) / 1e12, 2), "unit": "TFLOP/s",
+                "ms_per_step": round(fms, 4), "flops_per_step": fw["total"],
+                "down_tflops": round(fw["down"] / (down["avg_ms"] * 1e-3) / 1e12, 2) if down else None,
+                "kernels_ms": {k: round(v["avg_ms"], 4) for k, v in fkt.items()}})
     if not args.no_decode:
         dcfg = synth.CONFIGS[args.decode_workload]
         dms, dkt, lens = bench_decode(dcfg, max(args.steps, 10), args.warmup)

@@ -76,6 +76,27 @@ mla_status mla_latent_attn_fwd(const void* q, const void* kv_latent, const void*
                                int r, float scale, mla_dtype dt, void* workspace,
                                size_t workspace_bytes, void* stream);
 
+/* Bytes of workspace mla_latent_attn_fwd_full needs for this shape (0 on bad sizes). */
+size_t mla_latent_attn_full_workspace_size(int B, int T, int D, int H, int d, int r, mla_dtype dt);
+
+/* The full path in one call: the KV down-projection (page FW-GLM-5-1 l2_p1,
+ * operations list) writes the latent cache, then the causal prefill of
+ * mla_latent_attn_fwd runs over it (page FW-GLM-5-1 l2_p31):
+ *   kv_latent[b,t,:] = hidden[b,t,:] @ w_down,   out = attention(q, kv_latent).
+ *   hidden [B,T,D], w_down [D,r] (inputs), kv_latent [B,T,r] (OUTPUT: the
+ *   latent cache, stored in dt and then read back by the attention, so a
+ *   later decode can use it as its cache); the rest as mla_latent_attn_fwd.
+ * bf16 with D % 64 == 0 and r % 128 == 0 runs the down-projection on the
+ * matrix cores (bf16 operands, float32 accumulation); other shapes and
+ * float32 use the float32 vector path of mla_down_proj.  workspace must hold
+ * mla_latent_attn_full_workspace_size() bytes.  Equal, bit for bit, to
+ * mla_down_proj followed by mla_latent_attn_fwd when both take the vector
+ * down-projection path. */
+mla_status mla_latent_attn_fwd_full(const void* hidden, const void* w_down, const void* q, const void* w_up_k,
+                                    const void* w_up_v, void* kv_latent, void* out, int B, int T, int D, int H,
+                                    int d, int r, float scale, mla_dtype dt, void* workspace, size_t workspace_bytes,
+                                    void* stream);
+
 /* Bytes of workspace mla_latent_attn_fwd_masked needs for this shape (0 on bad sizes). */
 size_t mla_latent_attn_masked_workspace_size(int B, int T, int H, int d, int r, mla_dtype dt);
 

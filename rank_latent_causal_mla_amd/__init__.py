@@ -20,6 +20,7 @@ MLA_DTYPE_F32, MLA_DTYPE_BF16 = 0, 1
 
 EXPORTED = ("mla_down_proj", "mla_latent_attn_workspace_size", "mla_latent_attn_fwd",
             "mla_latent_attn_masked_workspace_size", "mla_latent_attn_fwd_masked",
+            "mla_latent_attn_full_workspace_size", "mla_latent_attn_fwd_full",
             "mla_latent_attn_unabsorbed_workspace_size", "mla_latent_attn_fwd_unabsorbed",
             "mla_decode_workspace_size", "mla_decode_fwd", "mla_decode_varlen_workspace_size",
             "mla_decode_varlen_fwd", "mla_kv_append", "mla_profile_enable", "mla_profile_collect",
@@ -58,6 +59,11 @@ def load():
     lib.mla_latent_attn_workspace_size.argtypes = [i32] * 6
     lib.mla_latent_attn_fwd.restype = i32
     lib.mla_latent_attn_fwd.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, i32, vp, sz, vp]
+    lib.mla_latent_attn_full_workspace_size.restype = sz
+    lib.mla_latent_attn_full_workspace_size.argtypes = [i32] * 7
+    lib.mla_latent_attn_fwd_full.restype = i32
+    lib.mla_latent_attn_fwd_full.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, i32, vp,
+                                             sz, vp]
     lib.mla_latent_attn_masked_workspace_size.restype = sz
     lib.mla_latent_attn_masked_workspace_size.argtypes = [i32] * 6
     lib.mla_latent_attn_fwd_masked.restype = i32
@@ -111,6 +117,16 @@ def mla_down_proj_raw(hidden, w_down, kv_latent, B, T, D, r, dt, stream=0):
 
 def mla_latent_attn_workspace_size(B, T, H, d, r, dt):
     return int(load().mla_latent_attn_workspace_size(B, T, H, d, r, dt))
+
+
+def mla_latent_attn_full_workspace_size(B, T, D, H, d, r, dt):
+    return int(load().mla_latent_attn_full_workspace_size(B, T, D, H, d, r, dt))
+
+
+def mla_latent_attn_fwd_full_raw(hidden, w_down, q, w_up_k, w_up_v, kv_latent, out, B, T, D, H, d, r, scale, dt, ws,
+                                 ws_bytes, stream=0):
+    return load().mla_latent_attn_fwd_full(hidden, w_down, q, w_up_k, w_up_v, kv_latent, out, B, T, D, H, d, r,
+                                           scale, dt, ws, ws_bytes, stream)
 
 
 def mla_latent_attn_masked_workspace_size(B, T, H, d, r, dt):
@@ -355,7 +371,35 @@ def mla_kv_append(kv_cache, seq_lens, new_latent, stream=None):
     return kv_cache
 
 
+def mla_latent_attn_fwd_full(hidden, w_down, q, w_up_k, w_up_v, kv_latent=None, out=None, scale=None,
+                             workspace=None, stream=None):
+    """Full path in one call: kv_latent[B,T,r] = hidden[B,T,D] @ w_down[D,r] (written: the latent
+    cache), then causal latent attention -> out[B,T,H,d].  Returns (out, kv_latent)."""
+    import torch
+    _dev(hidden, w_down, q, w_up_k, w_up_v)
+    B, T, H, d = q.shape
+    D, r = w_down.shape
+    if tuple(hidden.shape) != (B, T, D):
+        raise ValueError("hidden must be [B, T, D]")
+    dt = _dt(q)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if kv_latent is None:
+        kv_latent = torch.empty((B, T, r), dtype=q.dtype, device=q.device)
+    if out is None:
+        out = torch.empty_like(q)
+    nbytes = mla_latent_attn_full_workspace_size(B, T, D, H, d, r, dt)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    _dev(kv_latent, out, workspace)
+    _check(mla_latent_attn_fwd_full_raw(hidden.data_ptr(), w_down.data_ptr(), q.data_ptr(), w_up_k.data_ptr(),
+                                        w_up_v.data_ptr(), kv_latent.data_ptr(), out.data_ptr(), B, T, D, H, d, r,
+                                        float(scale), dt, workspace.data_ptr(),
+                                        workspace.numel() * workspace.element_size(), _stream(stream)))
+    return out, kv_latent
+
+
 def full_path(hidden, w_down, q, w_up_k, w_up_v, scale=None, stream=None):
-    """hidden -> kv_latent (mla_down_proj) -> causal latent attention (mla_latent_attn_fwd)."""
-    lat = mla_down_proj(hidden, w_down, stream=stream)
-    return mla_latent_attn_fwd(q, lat, w_up_k, w_up_v, scale=scale, stream=stream)
+    """hidden -> kv_latent -> causal latent attention, as one mla_latent_attn_fwd_full call."""
+    out, _ = mla_latent_attn_fwd_full(hidden, w_down, q, w_up_k, w_up_v, scale=scale, stream=stream)
+    return out

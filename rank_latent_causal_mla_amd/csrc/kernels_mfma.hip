@@ -608,6 +608,110 @@ void flash_latent_bf16(const uint16_t* __restrict__ q_lat, const uint16_t* __res
 }
 
 // ---------------------------------------------------------------------------
+// KV down-projection on the matrix cores (page FW-GLM-5-1 l2_p1, its
+// operations list: latent = hidden @ w_down): lat[m, rho] =
+// sum_k hid[m, k] w_down[k, rho], computed transposed, lat^T = W^T hid^T,
+// from wdT = w_down^T [R][D] so that both operands are rows with contiguous k.
+// Block: 128 latent columns (blockIdx.y) x 128 tokens (blockIdx.x); wave w
+// owns columns 64 (w & 1) .. + 63 and tokens 64 (w >> 1) .. + 63 as 2 x 2
+// tiles of 32 x 32.  k advances 32 at a time through two LDS buffers; the
+// next step's operands are loaded into registers while the current step's
+// matrix ops run.  Rows are padded to 40 elements (80 bytes), so the eight
+// lanes of a 16-byte read hit eight distinct groups of four banks.
+constexpr int kDownPad = 40;
+__global__ __launch_bounds__(256, 2) void down_bf16(const uint16_t* __restrict__ hid,
+                                                    const uint16_t* __restrict__ wdT, uint16_t* __restrict__ lat,
+                                                    int M, int D, int R) {
+  __shared__ __attribute__((aligned(16))) uint16_t sa[2][128 * kDownPad];  // W^T rows (latent columns)
+  __shared__ __attribute__((aligned(16))) uint16_t sb[2][128 * kDownPad];  // hidden rows (tokens)
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int g = lane >> 5, l32 = lane & 31;
+  const int m0 = blockIdx.x * 128, c0 = blockIdx.y * 128;
+  u32x4 ra[2], rb[2];
+  // chunk ch = tid + 256 i of a 128 x 32 tile: row ch / 4, elements 8 (ch % 4) .. + 7
+  auto load = [&](int k0) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int ch = tid + 256 * i, row = ch >> 2, part = ch & 3;
+      ra[i] = *(const u32x4*)(wdT + (size_t)(c0 + row) * D + k0 + 8 * part);
+      const int m = m0 + row < M ? m0 + row : M - 1;
+      rb[i] = *(const u32x4*)(hid + (size_t)m * D + k0 + 8 * part);
+    }
+  };
+  auto store = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int ch = tid + 256 * i, row = ch >> 2, part = ch & 3;
+      *(u32x4*)&sa[buf][row * kDownPad + 8 * part] = ra[i];
+      *(u32x4*)&sb[buf][row * kDownPad + 8 * part] = rb[i];
+    }
+  };
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int i2 = 0; i2 < 2; ++i2) acc[i][i2] = f32x16{};
+  const int nk = D / 32;
+  load(0);
+  store(0);
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    const int buf = kt & 1;
+    if (kt + 1 < nk) load(32 * (kt + 1));
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      bf16x8 a[2], b[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        a[i] = lds_read16(&sa[buf][(64 * (w & 1) + 32 * i + l32) * kDownPad + 16 * ks + 8 * g]);
+        b[i] = lds_read16(&sb[buf][(64 * (w >> 1) + 32 * i + l32) * kDownPad + 16 * ks + 8 * g]);
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int i2 = 0; i2 < 2; ++i2) acc[i][i2] = mfma32x32x16(a[i], b[i2], acc[i][i2]);
+    }
+    // buffer buf ^ 1 was last read in step kt - 1, before the barrier that ended it
+    if (kt + 1 < nk) store(buf ^ 1);
+    __syncthreads();
+  }
+  // acc[i][i2][4 j + v] = lat^T[c0 + 64 (w & 1) + 32 i + 8 j + 4 g + v][m0 + 64 (w >> 1) + 32 i2 + l32]
+#pragma unroll
+  for (int i2 = 0; i2 < 2; ++i2) {
+    const int m = m0 + 64 * (w >> 1) + 32 * i2 + l32;
+    if (m >= M) continue;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int rho = c0 + 64 * (w & 1) + 32 * i + 8 * j + 4 * g;
+        *(u32x2*)(lat + (size_t)m * R + rho) = u32x2{pack_bf16x2(acc[i][i2][4 * j], acc[i][i2][4 * j + 1]),
+                                                      pack_bf16x2(acc[i][i2][4 * j + 2], acc[i][i2][4 * j + 3])};
+      }
+  }
+}
+
+bool down_mfma_supported(int D, int r) { return D % 64 == 0 && r % 128 == 0 && r <= 1024; }
+
+size_t down_mfma_workspace(int D, int r) { return ((size_t)D * r * 2 + 255) / 256 * 256; }
+
+// w_down [D, r] -> w_down^T [r, D] in the workspace (the W_uv transpose with
+// R = D, H = 1, d = r), then the matrix-core product.
+hipError_t down_mfma(const uint16_t* hid, const uint16_t* wd, uint16_t* lat, int M, int D, int r, void* ws,
+                     hipStream_t st) {
+  uint16_t* wdT = (uint16_t*)ws;
+  hipError_t e;
+  {
+    ProfScope ps("transpose_wv", st);
+    e = transpose_wv_launch(wd, wdT, D, 1, r, st);
+    if (e != hipSuccess) return e;
+  }
+  ProfScope ps("down_bf16", st);
+  hipLaunchKernelGGL(down_bf16, dim3((M + 127) / 128, r / 128), dim3(256), 0, st, hid, wdT, lat, M, D, r);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
 // Key mask -> packed keys.  compact_scan: one block of 1024 per batch walks
 // key_mask[b] [T] bytes (nonzero = visible) in chunks of 1024 and writes
 // cnt[b][t] = number of visible keys s <= t and src[b][j] = the position of

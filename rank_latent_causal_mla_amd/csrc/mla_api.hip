@@ -110,14 +110,32 @@ size_t mla_latent_attn_masked_workspace_size(int B, int T, int H, int d, int r, 
   return use_mfma(dt, d, r) ? base + mla::key_mask_workspace(B, T, r) : base;
 }
 
+size_t mla_latent_attn_full_workspace_size(int B, int T, int D, int H, int d, int r, mla_dtype dt) {
+  if (D < 1) return 0;
+  const size_t attn = mla_latent_attn_workspace_size(B, T, H, d, r, dt);
+  if (attn == 0) return 0;
+  const size_t a = (attn + 255) / 256 * 256;
+  return dt == MLA_DTYPE_BF16 && mla::down_mfma_supported(D, r) ? a + mla::down_mfma_workspace(D, r) : a;
+}
+
 }  // extern "C"
 
 namespace {
 
-// Prefill with (key_mask) or without a key mask.
+// The producer of kv_latent in the full path: kv_latent = hidden @ w_down.
+struct DownProj {
+  const void* hidden;
+  const void* w_down;
+  int D;
+};
+
+// Prefill with (key_mask) or without a key mask; with `down`, kv_latent is
+// first written by the down-projection.  Every check runs before the first
+// launch.
 mla_status prefill_common(const void* q, const void* kv_latent, const uint8_t* key_mask, const void* w_up_k,
                           const void* w_up_v, void* out, int B, int T, int H, int d, int r, float scale,
-                          mla_dtype dt, void* workspace, size_t workspace_bytes, void* stream) {
+                          mla_dtype dt, void* workspace, size_t workspace_bytes, void* stream,
+                          const DownProj* down = nullptr) {
   if (!q || !kv_latent || !w_up_k || !w_up_v || !out || !workspace)
     return fail(MLA_ERR_INVALID_ARGUMENT, "null pointer");
   mla_status s = check_dims(B, T, H, d, r, dt, "T");
@@ -126,8 +144,16 @@ mla_status prefill_common(const void* q, const void* kv_latent, const uint8_t* k
   if (!aligned16(q) || !aligned16(kv_latent) || !aligned16(w_up_k) || !aligned16(w_up_v) ||
       !aligned16(out) || !aligned16(workspace))
     return fail(MLA_ERR_INVALID_ARGUMENT, "pointers must be 16-byte aligned");
-  const size_t need = key_mask ? mla_latent_attn_masked_workspace_size(B, T, H, d, r, dt)
-                               : mla_latent_attn_workspace_size(B, T, H, d, r, dt);
+  if (down) {
+    if (!down->hidden || !down->w_down) return fail(MLA_ERR_INVALID_ARGUMENT, "null pointer");
+    if (down->D < 1) return fail(MLA_ERR_INVALID_ARGUMENT, "D must be positive (got %d)", down->D);
+    if (!aligned16(down->hidden) || !aligned16(down->w_down))
+      return fail(MLA_ERR_INVALID_ARGUMENT, "pointers must be 16-byte aligned");
+    if ((double)B * T * down->D >= 9.0e15) return fail(MLA_ERR_UNSUPPORTED, "problem too large");
+  }
+  const size_t need = down ? mla_latent_attn_full_workspace_size(B, T, down->D, H, d, r, dt)
+                      : key_mask ? mla_latent_attn_masked_workspace_size(B, T, H, d, r, dt)
+                                 : mla_latent_attn_workspace_size(B, T, H, d, r, dt);
   if (workspace_bytes < need)
     return fail(MLA_ERR_WORKSPACE, "workspace %zu bytes < %zu required", workspace_bytes, need);
   hipStream_t st = (hipStream_t)stream;
@@ -138,6 +164,17 @@ mla_status prefill_common(const void* q, const void* kv_latent, const uint8_t* k
     if (mla::flash_lds_bytes(r) > limit)
       return fail(MLA_ERR_UNSUPPORTED, "prefill needs %zu bytes of LDS per block, device allows %zu",
                   mla::flash_lds_bytes(r), limit);
+  }
+  if (down) {
+    hipError_t e;
+    if (dt == MLA_DTYPE_BF16 && mla::down_mfma_supported(down->D, r)) {
+      const size_t a = (mla_latent_attn_workspace_size(B, T, H, d, r, dt) + 255) / 256 * 256;
+      e = mla::down_mfma((const uint16_t*)down->hidden, (const uint16_t*)down->w_down, (uint16_t*)kv_latent, B * T,
+                         down->D, r, (char*)workspace + a, st);
+    } else {
+      e = mla::down_proj(dt == MLA_DTYPE_BF16, down->hidden, down->w_down, (void*)kv_latent, B * T, down->D, r, st);
+    }
+    if (e != hipSuccess) return launched(e, "down-projection launch");
   }
   if (use_mfma(dt, d, r))
     return launched(mla::prefill_mfma(q, kv_latent, w_up_k, w_up_v, out, B, T, H, d, r,
@@ -158,6 +195,15 @@ mla_status mla_latent_attn_fwd(const void* q, const void* kv_latent, const void*
                                void* stream) {
   return prefill_common(q, kv_latent, nullptr, w_up_k, w_up_v, out, B, T, H, d, r, scale, dt, workspace,
                         workspace_bytes, stream);
+}
+
+mla_status mla_latent_attn_fwd_full(const void* hidden, const void* w_down, const void* q, const void* w_up_k,
+                                    const void* w_up_v, void* kv_latent, void* out, int B, int T, int D, int H,
+                                    int d, int r, float scale, mla_dtype dt, void* workspace, size_t workspace_bytes,
+                                    void* stream) {
+  const DownProj down{hidden, w_down, D};
+  return prefill_common(q, kv_latent, nullptr, w_up_k, w_up_v, out, B, T, H, d, r, scale, dt, workspace,
+                        workspace_bytes, stream, &down);
 }
 
 mla_status mla_latent_attn_fwd_masked(const void* q, const void* kv_latent, const uint8_t* key_mask,

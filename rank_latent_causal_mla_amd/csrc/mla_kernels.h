@@ -69,6 +69,13 @@ size_t decode_simt_workspace(int B, int Tmax, int H, int d, int r);
 hipError_t kv_append(bool dt_bf16, void* kv_cache, int32_t* lens, const void* new_latent, int B, int Tmax, int r,
                      hipStream_t st);
 
+// ---- bf16 down-projection on the matrix cores (D % 64 == 0, r % 128 == 0):
+// latent [M, r] = hid [M, D] w_down [D, r]; ws holds down_mfma_workspace() bytes (w_down^T)
+bool down_mfma_supported(int D, int r);
+size_t down_mfma_workspace(int D, int r);
+hipError_t down_mfma(const uint16_t* hid, const uint16_t* wd, uint16_t* lat, int M, int D, int r, void* ws,
+                     hipStream_t st);
+
 // ---- down-projection (any sizes), float32 accumulation
 hipError_t down_proj(bool dt_bf16, const void* hidden, const void* w_down, void* latent, int M,
                      int D, int r, hipStream_t st);

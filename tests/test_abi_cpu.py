@@ -210,3 +210,44 @@ def test_masked_workspace_size():
     assert mla.mla_latent_attn_masked_workspace_size(2, 64, 4, 32, 32, F32) == \
         mla.mla_latent_attn_workspace_size(2, 64, 4, 32, 32, F32)
     assert mla.mla_latent_attn_masked_workspace_size(0, 64, 4, 32, 32, F32) == 0
+
+
+def full(**kw):
+    a = dict(hid=P, wd=P, q=P, wk=P, wv=P, kv=P, out=P, B=2, T=64, D=256, H=4, d=32, r=32, scale=0.17, dt=F32, ws=P,
+             wsb=1 << 40)
+    a.update(kw)
+    return mla.mla_latent_attn_fwd_full_raw(a["hid"], a["wd"], a["q"], a["wk"], a["wv"], a["kv"], a["out"], a["B"],
+                                            a["T"], a["D"], a["H"], a["d"], a["r"], a["scale"], a["dt"], a["ws"],
+                                            a["wsb"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    ({"hid": 0}, mla.MLA_ERR_INVALID_ARGUMENT),
+    ({"wd": 0}, mla.MLA_ERR_INVALID_ARGUMENT),
+    ({"kv": 0}, mla.MLA_ERR_INVALID_ARGUMENT),
+    ({"D": 0}, mla.MLA_ERR_INVALID_ARGUMENT),
+    ({"hid": P + 4}, mla.MLA_ERR_INVALID_ARGUMENT),
+    ({"wd": P + 8}, mla.MLA_ERR_INVALID_ARGUMENT),
+    ({"T": 0}, mla.MLA_ERR_INVALID_ARGUMENT),
+    ({"scale": float("inf")}, mla.MLA_ERR_INVALID_ARGUMENT),
+    ({"r": 2048}, mla.MLA_ERR_UNSUPPORTED),
+    ({"wsb": 100}, mla.MLA_ERR_WORKSPACE),
+])
+def test_full_argument_errors(kw, status):
+    assert full(**kw) == status
+    assert mla.last_error() != ""
+
+
+def test_full_workspace_size():
+    # bf16 matrix-core down-projection: the attention workspace, then w_down^T [r][D] bf16
+    base = mla.mla_latent_attn_workspace_size(8, 2048, 16, 128, 512, BF16)
+    assert mla.mla_latent_attn_full_workspace_size(8, 2048, 1024, 16, 128, 512, BF16) == base + 1024 * 512 * 2
+    # float32 and D % 64 != 0: the vector down-projection needs no scratch
+    assert mla.mla_latent_attn_full_workspace_size(4, 512, 1024, 8, 64, 128, F32) == \
+        mla.mla_latent_attn_workspace_size(4, 512, 8, 64, 128, F32)
+    assert mla.mla_latent_attn_full_workspace_size(2, 50, 96, 4, 128, 128, BF16) == \
+        mla.mla_latent_attn_workspace_size(2, 50, 4, 128, 128, BF16)
+    assert mla.mla_latent_attn_full_workspace_size(2, 50, 0, 4, 128, 128, BF16) == 0
+    # the workspace test above must pass with the full requirement, not the attention one
+    need = mla.mla_latent_attn_full_workspace_size(2, 64, 1024, 4, 128, 512, BF16)
+    assert full(dt=BF16, d=128, r=512, D=1024, wsb=need - 1) == mla.MLA_ERR_WORKSPACE
