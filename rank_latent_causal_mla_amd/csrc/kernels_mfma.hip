@@ -43,6 +43,12 @@ __device__ __forceinline__ int qswz(int c, int s) {
   else return c ^ ((s / (16 / NCd)) & (NCd - 1));
 }
 
+// The results of a row block (32 rows x the block's 128 NB columns) are
+// staged in LDS and stored as whole row segments, 16 bytes a lane: the matrix
+// layout leaves each lane four consecutive columns of one row, and storing
+// those directly scatters every instruction over 32 rows.  Staged rows are
+// padded by 16 bytes, so the 16 lanes of an 8-byte staging write (rows
+// 0..15 of one column) fall on distinct bank pairs but for rows r and r + 8.
 template <int R, int DK>
 __global__ __launch_bounds__(256, 2) void absorb_bf16(const uint16_t* __restrict__ q,
                                                       const uint16_t* __restrict__ wk,
@@ -55,8 +61,13 @@ __global__ __launch_bounds__(256, 2) void absorb_bf16(const uint16_t* __restrict
   constexpr int RPI = 64 / NCd;                       // rows per copy instruction
   constexpr int NINS = TB / 1024;                     // copy instructions per row block
   constexpr int NIW = NINS >= 4 ? NINS / 4 : 1;       // at most, per wave
+  constexpr int RB = 128 * NB;                        // columns of the block
+  constexpr int OS = RB * 2 + 16;                     // staged row stride, bytes
+  constexpr int OCH = RB / 8;                         // 16-byte chunks of a staged row
   static_assert(NCd <= 64 && 64 % NCd == 0 && TB % 1024 == 0, "copies cover whole rows");
+  static_assert((32 * OCH) % 256 == 0, "the block's threads share the staged chunks evenly");
   __shared__ __attribute__((aligned(16))) char buf[2][TB];
+  __shared__ __attribute__((aligned(16))) char ostage[32 * OS];
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane >> 5, l32 = lane & 31;
@@ -113,20 +124,27 @@ __global__ __launch_bounds__(256, 2) void absorb_bf16(const uint16_t* __restrict
 #pragma unroll
       for (int ks = 0; ks < DK; ++ks) acc[i] = mfma32x32x16(a[i][ks], bq[ks], acc[i]);
     }
-    const int n = 32 * (nb0 + k) + l32;
-    if (n < N) {
-      uint16_t* orow = q_lat + ((size_t)n * H + h) * R;
+    // stage: lane (g, l32) holds columns 32 i + 8 j + 4 g .. + 3 (of the
+    // wave's 32 NB) of row l32
 #pragma unroll
-      for (int i = 0; i < NB; ++i)
+    for (int i = 0; i < NB; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int rho = rho0 + 32 * i + 8 * j + 4 * g;
-          u32x2 v = {pack_bf16x2(acc[i][4 * j] * qscale, acc[i][4 * j + 1] * qscale),
-                     pack_bf16x2(acc[i][4 * j + 2] * qscale, acc[i][4 * j + 3] * qscale)};
-          *(u32x2*)(orow + rho) = v;
-        }
+      for (int j = 0; j < 4; ++j) {
+        const int col = w * 32 * NB + 32 * i + 8 * j + 4 * g;
+        *(__attribute__((address_space(3))) u32x2*)(uintptr_t)(ostage + l32 * OS + 2 * col) =
+            u32x2{pack_bf16x2(acc[i][4 * j] * qscale, acc[i][4 * j + 1] * qscale),
+                  pack_bf16x2(acc[i][4 * j + 2] * qscale, acc[i][4 * j + 3] * qscale)};
+      }
+    lds_publish_barrier();  // the row block's results are staged
+    // store: chunk c = tid + 256 u is row c / OCH, 16-byte piece c % OCH
+#pragma unroll
+    for (int u = 0; u < 32 * OCH / 256; ++u) {
+      const int c = threadIdx.x + 256 * u, row = c / OCH, piece = c % OCH;
+      const int n = 32 * (nb0 + k) + row;
+      const u32x4 v = *(const __attribute__((address_space(3))) u32x4*)(uintptr_t)(ostage + row * OS + 16 * piece);
+      if (n < N) *(u32x4*)(q_lat + ((size_t)n * H + h) * R + 128 * NB * blockIdx.z + 8 * piece) = v;
     }
-    __builtin_amdgcn_s_barrier();  // buffer k & 1 is refilled next iteration
+    __builtin_amdgcn_s_barrier();  // buffer k & 1 is refilled and the stage rewritten next iteration
   }
 }
 
