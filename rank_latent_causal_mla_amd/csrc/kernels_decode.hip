@@ -163,7 +163,6 @@ void decode_split(const uint16_t* __restrict__ q_lat, const uint16_t* __restrict
     lsum += __shfl_xor(lsum, 32);
     if (G == 0) lbuf[(kb * 2 + qb) * 16 + n] = lsum;
     lds_publish_barrier();
-    mfma_agpr_wait();
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
       const float lt = lbuf[q * 16 + n] + lbuf[(2 + q) * 16 + n];
@@ -174,7 +173,6 @@ void decode_split(const uint16_t* __restrict__ q_lat, const uint16_t* __restrict
       uint16_t* po = part_o + prow * R + rw + 4 * G;
 #pragma unroll
       for (int c = 0; c < NCW; ++c) {
-        mfma_agpr_tie(o[c][q]);
         const u32x2 v = {pack_bf16x2(o[c][q][0] * inv, o[c][q][1] * inv),
                          pack_bf16x2(o[c][q][2] * inv, o[c][q][3] * inv)};
         *(u32x2*)(po + 16 * c) = v;
@@ -240,15 +238,10 @@ void decode_split(const uint16_t* __restrict__ q_lat, const uint16_t* __restrict
     if (tau + 1 < issued) dma_wait_tiles<NI>(issued - tau - 2);
     lds_publish_barrier();  // Y: P of tile tau complete; tile tau + 1 landed
     if (__builtin_amdgcn_ballot_w64(grow_any)) {
-      mfma_agpr_wait();
 #pragma unroll
       for (int c = 0; c < NCW; ++c)
 #pragma unroll
-        for (int q = 0; q < 2; ++q) {
-          mfma_agpr_tie(o[c][q]);
-          o[c][q] *= alpha[q];
-          mfma_agpr_tie(o[c][q]);
-        }
+        for (int q = 0; q < 2; ++q) o[c][q] *= alpha[q];
     }
     // ---- O^T += L^T P^T over this wave's columns.  Transpose read t of lane
     // (G, n): key 16 t + 4 G + n / 4, columns rw + 16 c + 4 (n % 4) .. + 3.
@@ -266,8 +259,8 @@ void decode_split(const uint16_t* __restrict__ q_lat, const uint16_t* __restrict
                                                          __builtin_bit_cast(u32x2, a2[0])[1],
                                                          __builtin_bit_cast(u32x2, a2[1])[0],
                                                          __builtin_bit_cast(u32x2, a2[1])[1]});
-      mfma16x16x32_a(o[c][0], av, Pq[0]);
-      mfma16x16x32_a(o[c][1], av, Pq[1]);
+      o[c][0] = mfma16x16x32(av, Pq[0], o[c][0]);
+      o[c][1] = mfma16x16x32(av, Pq[1], o[c][1]);
     }
     // ---- advance; at the end of a segment, its partial state and the next query
     ck += kDecodeTileKeys;
