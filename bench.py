@@ -29,6 +29,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2516.6     # 256 CU x 2.4 GHz x 4096 dense bf16 FLOP/clk/CU
 PEAK_HBM_GBS = 8000.0         # HBM3E
+PEAK_FP32_TFLOPS = 157.3      # 256 CU x 2.4 GHz x 256 fp32 FLOP/clk/CU (vector ALUs)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 
 
@@ -347,7 +348,12 @@ def main(argv=None):
                     "masked keys are skipped; value counts the visible causal keys only",
             "value": round(mw["total"] / (mms * 1e-3) / 1e12, 2), "unit": "TFLOP/s",
             "ms_per_step": round(mms, 4), "flops_per_step": mw["total"],
-            "flash_tflops": round(mw["attn"] / (mflash["avg_ms"] * 1e-3) / 1e12, 2) if mflash else None,
+            "roofline": None if not mflash else {
+                "bound": "mfma", "achieved": round(mw["attn"] / (mflash["avg_ms"] * 1e-3) / 1e12, 2),
+                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(mw["attn"] / (mflash["avg_ms"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                "traffic": measured_traffic("flash_latent_bf16_masked"), "kernel": "flash_latent_bf16_masked",
+                "avg_ms": round(mflash["avg_ms"], 4), "flops_per_launch": mw["attn"]},
             "kernels_ms": {k: round(v["avg_ms"], 4) for k, v in mkt.items()}}
     if not args.no_full:
         import dataclasses
@@ -357,6 +363,18 @@ def main(argv=None):
             fms, fkt = bench_full(fcfg, args.steps, args.warmup)
             fw = prefill_flops(fcfg)
             down = fkt.get("down_bf16") or fkt.get("gemm_simt")
+            if fcfg.dtype == "bf16":
+                dom, dom_flops, bound, peak = fkt.get("flash_latent_bf16"), fw["attn"], "mfma", PEAK_BF16_TFLOPS
+                dom_name = "flash_latent_bf16"
+            else:   # float32: every product on the vector ALUs
+                dom, dom_flops, bound, peak = fkt.get("attend_simt"), fw["attn"], "alu", PEAK_FP32_TFLOPS
+                dom_name = "attend_simt"
+            froof = None
+            if dom:
+                ach = dom_flops / (dom["avg_ms"] * 1e-3) / 1e12
+                froof = {"bound": bound, "achieved": round(ach, 2), "peak": peak, "unit": "TFLOP/s",
+                         "frac": round(ach / peak, 4), "traffic": None, "kernel": dom_name,
+                         "avg_ms": round(dom["avg_ms"], 4), "flops_per_launch": dom_flops}
             line["full_path"].append({
                 "what": "mla_latent_attn_fwd_full: kv_latent = hidden @ w_down written as the latent cache, then the "
                         "causal prefill; value counts the down-projection and the absorbed-method FLOPs",
@@ -365,6 +383,7 @@ def main(argv=None):
                 "value": round(fw["total"] / (fms * 1e-3) / 1e12, 2), "unit": "TFLOP/s",
                 "ms_per_step": round(fms, 4), "flops_per_step": fw["total"],
                 "down_tflops": round(fw["down"] / (down["avg_ms"] * 1e-3) / 1e12, 2) if down else None,
+                "roofline": froof,
                 "kernels_ms": {k: round(v["avg_ms"], 4) for k, v in fkt.items()}})
     if not args.no_decode:
         dcfg = synth.CONFIGS[args.decode_workload]

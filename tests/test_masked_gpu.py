@@ -127,3 +127,31 @@ def test_bf16_prefill_full_size_masked_sampled():
     for b in range(cfg.B):
         first = int(np.argmin(mask[b])) if not mask[b].all() else T
         assert torch.equal(out[b, :first].view(torch.int16), unmasked[b, :first].view(torch.int16)), b
+
+
+def test_bf16_long_prefill_masked_sampled():
+    """bf16_long_prefill (the benchmarked workload) with the benchmark's mask:
+    sampled rows of both batches against the oracle, including rows past a
+    batch's valid length (they attend its visible keys only)."""
+    import torch
+    cfg = synth.CONFIGS["bf16_long_prefill"]
+    inp = synth.make_inputs(cfg)
+    mask = synth.make_key_mask(cfg, p_hole=0.05)
+    print(f"full-size masked prefill {cfg.name}", flush=True)
+    out, _ = run_masked(cfg, inp, mask)
+    rng = np.random.default_rng(9)
+    T = cfg.T
+    rb, rh, rt = [], [], []
+    for (b, h) in [(0, 0), (1, 63), (1, 17)]:
+        last = int(np.nonzero(mask[b])[0].max())
+        for t in sorted(set([0, 31, 32, 4095, last - 1, last, min(last + 1, T - 1), T - 1] +
+                            list(rng.integers(0, T, 10)))):
+            rb.append(b); rh.append(h); rt.append(t)
+    rb, rh, rt = map(np.array, (rb, rh, rt))
+    ref = oracle.attend_rows(inp["q"][rb, rt, rh], rb, rh, rt + 1, inp["kv_latent"], inp["w_up_k"], inp["w_up_v"],
+                             cfg.scale, key_mask=mask)
+    got = to_f64(out[torch.from_numpy(rb).cuda(), torch.from_numpy(rt).cuda(), torch.from_numpy(rh).cuda()])
+    err = compare_nan(got, ref, cfg.dtype, cfg.name)
+    rel = float(np.sqrt(np.nanmean((got - ref) ** 2) / np.nanmean(ref ** 2)))
+    print(f"{len(rb)} sampled rows, max abs err {err:.3e}, rel rms {rel:.3e}")
+    assert rel < 4e-3
