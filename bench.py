@@ -275,6 +275,7 @@ def main(argv=None):
     ap.add_argument("--no-unabsorbed", action="store_true", help="skip the unabsorbed prefill timing")
     ap.add_argument("--no-masked", action="store_true", help="skip the key-masked prefill timing")
     ap.add_argument("--no-full", action="store_true", help="skip the full-path (down-projection + prefill) timing")
+    ap.add_argument("--no-short", action="store_true", help="skip the bf16_prefill (T=2048) timing")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (reference for HBM byte counters)")
     args = ap.parse_args(argv)
@@ -321,6 +322,22 @@ def main(argv=None):
         "roofline": roof,
         "kernels_ms": {k: round(v["avg_ms"], 4) for k, v in kt.items()},
     }
+    if args.workload == "bf16_long_prefill" and not args.no_short:
+        # the shorter bf16 prefill workload (B=8, T=2048, H=16): the same kernels at a length where each query
+        # block carries 8x less work, so fixed costs per block weigh more
+        scfg = synth.CONFIGS["bf16_prefill"]
+        sms, skt, _ = bench_prefill(scfg, args.steps, args.warmup)
+        sw = prefill_flops(scfg)
+        sfl = skt.get("flash_latent_bf16")
+        line["prefill_short"] = {
+            "workload": scfg.name, "value": round(sw["total"] / (sms * 1e-3) / 1e12, 2), "unit": "TFLOP/s",
+            "ms_per_step": round(sms, 4), "flops_per_step": sw["total"],
+            "roofline": None if not sfl else {
+                "bound": "mfma", "achieved": round(sw["attn"] / (sfl["avg_ms"] * 1e-3) / 1e12, 2),
+                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(sw["attn"] / (sfl["avg_ms"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                "kernel": "flash_latent_bf16", "avg_ms": round(sfl["avg_ms"], 4), "flops_per_launch": sw["attn"]},
+            "kernels_ms": {k: round(v["avg_ms"], 4) for k, v in skt.items()}}
     if not args.no_unabsorbed and cfg.dtype == "bf16" and \
             mla.mla_latent_attn_unabsorbed_workspace_size(cfg.B, cfg.T, cfg.H, cfg.d, cfg.r, mla.MLA_DTYPE_BF16):
         ums, ukt, _ = bench_prefill(cfg, args.steps, args.warmup, unabsorbed=True)

@@ -218,6 +218,12 @@ def _dev(*ts):
             raise ValueError("tensors must be contiguous")
 
 
+def _shaped(t, shape, dtype, name):
+    """A caller-supplied output must have exactly the shape and dtype the call writes."""
+    if tuple(t.shape) != tuple(shape) or t.dtype != dtype:
+        raise ValueError(f"{name} must be {list(shape)} {dtype}, got {list(t.shape)} {t.dtype}")
+
+
 def mla_down_proj(hidden, w_down, kv_latent=None, stream=None):
     """kv_latent[B,T,r] = hidden[B,T,D] @ w_down[D,r]."""
     import torch
@@ -226,6 +232,7 @@ def mla_down_proj(hidden, w_down, kv_latent=None, stream=None):
     r = w_down.shape[1]
     if kv_latent is None:
         kv_latent = torch.empty((B, T, r), dtype=hidden.dtype, device=hidden.device)
+    _shaped(kv_latent, (B, T, r), hidden.dtype, "kv_latent")
     _dev(kv_latent)
     _check(mla_down_proj_raw(hidden.data_ptr(), w_down.data_ptr(), kv_latent.data_ptr(), B, T, D, r,
                              _dt(hidden), _stream(stream)))
@@ -243,6 +250,7 @@ def mla_latent_attn_fwd(q, kv_latent, w_up_k, w_up_v, out=None, scale=None, work
         scale = 1.0 / math.sqrt(d)
     if out is None:
         out = torch.empty_like(q)
+    _shaped(out, q.shape, q.dtype, "out")
     nbytes = mla_latent_attn_workspace_size(B, T, H, d, r, dt)
     if workspace is None:
         workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
@@ -272,6 +280,7 @@ def mla_latent_attn_fwd_masked(q, kv_latent, key_mask, w_up_k, w_up_v, out=None,
         scale = 1.0 / math.sqrt(d)
     if out is None:
         out = torch.empty_like(q)
+    _shaped(out, q.shape, q.dtype, "out")
     nbytes = mla_latent_attn_masked_workspace_size(B, T, H, d, r, dt)
     if workspace is None:
         workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
@@ -295,6 +304,7 @@ def mla_latent_attn_fwd_unabsorbed(q, kv_latent, w_up_k, w_up_v, out=None, scale
         scale = 1.0 / math.sqrt(d)
     if out is None:
         out = torch.empty_like(q)
+    _shaped(out, q.shape, q.dtype, "out")
     nbytes = mla_latent_attn_unabsorbed_workspace_size(B, T, H, d, r, dt)
     if workspace is None:
         workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
@@ -319,6 +329,7 @@ def mla_decode_fwd(q, kv_latent, seq_lens, w_up_k, w_up_v, out=None, scale=None,
         scale = 1.0 / math.sqrt(d)
     if out is None:
         out = torch.empty_like(q)
+    _shaped(out, q.shape, q.dtype, "out")
     nbytes = mla_decode_workspace_size(B, Tmax, H, d, r, dt)
     if workspace is None:
         workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
@@ -346,6 +357,7 @@ def mla_decode_varlen_fwd(q, kv_latent, cu_seqlens, w_up_k, w_up_v, out=None, sc
         scale = 1.0 / math.sqrt(d)
     if out is None:
         out = torch.empty_like(q)
+    _shaped(out, q.shape, q.dtype, "out")
     nbytes = mla_decode_varlen_workspace_size(B, total, H, d, r, dt)
     if workspace is None:
         workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
@@ -386,8 +398,10 @@ def mla_latent_attn_fwd_full(hidden, w_down, q, w_up_k, w_up_v, kv_latent=None, 
         scale = 1.0 / math.sqrt(d)
     if kv_latent is None:
         kv_latent = torch.empty((B, T, r), dtype=q.dtype, device=q.device)
+    _shaped(kv_latent, (B, T, r), q.dtype, "kv_latent")
     if out is None:
         out = torch.empty_like(q)
+    _shaped(out, q.shape, q.dtype, "out")
     nbytes = mla_latent_attn_full_workspace_size(B, T, D, H, d, r, dt)
     if workspace is None:
         workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
