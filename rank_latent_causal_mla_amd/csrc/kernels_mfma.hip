@@ -29,7 +29,7 @@ namespace mla {
 // registers) and kAbsorbRowBlocks row blocks of 32 queries, whose q rows are
 // copied into LDS once per block by LDS-DMA (two buffers, the next copy in
 // flight), chunk-swizzled so the operand reads are conflict-free.
-constexpr int kAbsorbRowBlocks = 8;
+constexpr int kAbsorbRowBlocks = 32;
 template <int R, int DK>
 constexpr int absorb_nb() { return R / 128 < 32 / DK ? R / 128 : 32 / DK; }
 
@@ -194,7 +194,7 @@ hipError_t transpose_wv_launch(const uint16_t* wv, uint16_t* wvT, int R, int H, 
 // o_lat rows of a row block are copied once per block into LDS by LDS-DMA
 // (two buffers, the next block's copy in flight), chunk-swizzled by the row
 // so the four waves' operand reads are conflict-free.
-constexpr int kUpRowBlocks = 8;
+constexpr int kUpRowBlocks = 32;
 template <int R>
 constexpr size_t up_lds_bytes() { return (size_t)2 * 32 * R * 2; }
 
