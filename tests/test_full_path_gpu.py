@@ -41,6 +41,7 @@ CASES = [
     ("bf16_prefill", dict(B=1, T=300, H=2, d=64, r=128, D=256)),               # ragged 128-token blocks
     ("bf16_prefill", dict(B=2, T=70, H=4, r=256, D=192)),
     ("bf16_prefill", dict(B=2, T=50, H=4, r=128, D=96)),                       # D % 64 != 0: vector path
+    ("bf16_prefill", dict(B=3, T=1, H=2, d=32, r=128, D=64)),                  # 3 tokens: one ragged block
 ]
 
 

@@ -50,6 +50,7 @@ CASES = [
     ("bf16_prefill", dict(B=2, T=70, H=2, r=128, d=64), dict(p_hole=0.3, lead=33)),
     ("bf16_prefill", dict(B=1, T=40, H=4, r=48, d=16), dict(p_hole=0.3, lead=0)),  # bf16 outside the tiles
     ("fp32_small", dict(T=129, r=512, d=128, H=2), dict(p_hole=0.2, lead=2)),
+    ("bf16_prefill", dict(B=4, T=1, H=16), dict(p_hole=0.5, lead=1)),          # single key: v_0 or NaN
 ]
 
 
