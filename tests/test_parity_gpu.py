@@ -60,6 +60,8 @@ SMALL = [
     ("bf16_prefill", dict(B=2, T=65, H=2, r=128, d=64)),       # r = 128, d = 64
     ("bf16_prefill", dict(B=1, T=40, H=4, r=48, d=16)),        # bf16 outside the matrix-core tiles
     ("fp32_small", dict(T=129, r=512, d=128, H=2)),            # float32 at the wide latent
+    ("bf16_prefill", dict(B=1, T=70, H=4, d=256)),             # d = 256: absorption in two rank halves
+    ("bf16_prefill", dict(B=2, T=40, H=8, d=32, r=128)),       # d = 32
 ]
 
 
@@ -182,6 +184,8 @@ DECODE_SMALL = [
     ("bf16_decode", dict(B=3, T=2100, H=8), [1025, 2100, 1024]),       # splits, partial last split
     ("bf16_decode", dict(B=2, T=64, H=40), [64, 7]),                   # two head groups, ragged
     ("bf16_decode", dict(B=2, T=50, H=4, r=48, d=16), [50, 1]),        # outside matrix-core tiles
+    ("bf16_decode", dict(B=3, T=700, H=16, d=256), [700, 1, 333]),     # d = 256
+    ("bf16_decode", dict(B=2, T=300, H=32, d=64, r=256), [300, 129]),  # d = 64, r = 256
     ("fp32_small", dict(B=3, T=70, decode=True), [70, 1, 33]),         # float32 decode
 ]
 
