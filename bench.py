@@ -384,8 +384,8 @@ def main(argv=None):
                 dom, dom_flops, bound, peak = fkt.get("flash_latent_bf16"), fw["attn"], "mfma", PEAK_BF16_TFLOPS
                 dom_name = "flash_latent_bf16"
             else:   # float32: every product on the vector ALUs
-                dom, dom_flops, bound, peak = fkt.get("attend_simt"), fw["attn"], "alu", PEAK_FP32_TFLOPS
-                dom_name = "attend_simt"
+                dom_name = "attend_f32_tiled" if "attend_f32_tiled" in fkt else "attend_simt"
+                dom, dom_flops, bound, peak = fkt.get(dom_name), fw["attn"], "alu", PEAK_FP32_TFLOPS
             froof = None
             if dom:
                 ach = dom_flops / (dom["avg_ms"] * 1e-3) / 1e12

@@ -122,6 +122,172 @@ __global__ void attend_simt(const float* __restrict__ q_lat, const T* __restrict
   }
 }
 
+// Causal prefill attention over the latents, float32, tiled: one block per
+// 64 consecutive rows (t*H + h) of a batch and 64-key tiles, both staged in
+// LDS and shared by the block.  Thread (rg, cg) = (tid / 16, tid % 16) owns
+// rows rg + 16 i (i = 0..3): for the scores, keys cg + 16 j of the tile
+// (j = 0..3); for the output, latent columns 4 (cg + 16 c) .. + 3
+// (c < R / 64).  The 16 threads of a row group hold the same running max and
+// sum (reduced over the group by shuffles), so the online rescale needs no
+// exchange; the probabilities go through LDS to the output product.  Rows
+// are padded to R + 4 floats: consecutive rows start in consecutive 16-byte
+// bank groups.  R in {64, 128, 256}.
+constexpr int kF32Rows = 64, kF32Keys = 64;
+template <int R>
+constexpr size_t attend_f32_lds_bytes() { return (size_t)(2 * 64 * (R + 4) + 64 * (kF32Keys + 4)) * 4; }
+
+template <typename T>
+__device__ __forceinline__ float4 ld4(const T* p);
+template <>
+__device__ __forceinline__ float4 ld4<float>(const float* p) { return *(const float4*)p; }
+template <>
+__device__ __forceinline__ float4 ld4<uint16_t>(const uint16_t* p) {
+  const u32x2 v = *(const u32x2*)p;
+  return float4{__uint_as_float(v[0] << 16), __uint_as_float(v[0] & 0xFFFF0000u), __uint_as_float(v[1] << 16),
+                __uint_as_float(v[1] & 0xFFFF0000u)};
+}
+
+template <int R, typename T>
+__global__ __launch_bounds__(256) void attend_f32_tiled(const float* __restrict__ q_lat, const T* __restrict__ lat,
+                                                        float* __restrict__ o_lat, int Tn, int H, float sl2) {
+  constexpr int QS = R + 4;        // row stride (floats) of the q and latent tiles
+  constexpr int PS = kF32Keys + 4; // row stride of the probabilities
+  constexpr int NC = R / 64;       // 4-column chunks per thread in the output
+  extern __shared__ __attribute__((aligned(16))) float sm[];
+  float* qs = sm;
+  float* ls = qs + kF32Rows * QS;
+  float* ps = ls + kF32Keys * QS;
+  const int tid = threadIdx.x, rg = tid >> 4, cg = tid & 15;
+  const int b = blockIdx.y;
+  const long TH = (long)Tn * H;
+  const long row0 = (long)blockIdx.x * kF32Rows;
+  for (int idx = tid; idx < kF32Rows * (R / 4); idx += 256) {
+    const int r = idx / (R / 4), c = idx % (R / 4);
+    const long row = row0 + r < TH ? row0 + r : TH - 1;
+    *(float4*)&qs[r * QS + 4 * c] = *(const float4*)&q_lat[((size_t)b * TH + row) * R + 4 * c];
+  }
+  const long last = row0 + kF32Rows - 1 < TH - 1 ? row0 + kF32Rows - 1 : TH - 1;
+  const int ntiles = (int)(last / H) / kF32Keys + 1;
+  int trow[4];
+  float m[4], l[4];
+  float4 o[4][NC];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const long row = row0 + rg + 16 * i < TH ? row0 + rg + 16 * i : TH - 1;
+    trow[i] = (int)(row / H);
+    m[i] = -INFINITY;
+    l[i] = 0.f;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) o[i][c] = float4{0.f, 0.f, 0.f, 0.f};
+  }
+  const T* latb = lat + (size_t)b * Tn * R;
+  for (int kt = 0; kt < ntiles; ++kt) {
+    const int k0 = kt * kF32Keys;
+    __syncthreads();  // the previous tile's products are done with ls and ps
+    for (int idx = tid; idx < kF32Keys * (R / 4); idx += 256) {
+      const int k = idx / (R / 4), c = idx % (R / 4);
+      const int s = k0 + k < Tn ? k0 + k : Tn - 1;
+      *(float4*)&ls[k * QS + 4 * c] = ld4<T>(latb + (size_t)s * R + 4 * c);
+    }
+    __syncthreads();
+    float sc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) sc[i][j] = 0.f;
+#pragma unroll 4
+    for (int rho = 0; rho < R; rho += 4) {
+      float4 qv[4], lv[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) qv[i] = *(const float4*)&qs[(rg + 16 * i) * QS + rho];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) lv[j] = *(const float4*)&ls[(cg + 16 * j) * QS + rho];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          sc[i][j] += qv[i].x * lv[j].x + qv[i].y * lv[j].y + qv[i].z * lv[j].z + qv[i].w * lv[j].w;
+    }
+    // causal mask, then the online update of each row (keys s <= t only)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float x[4], mx = -INFINITY;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        x[j] = k0 + cg + 16 * j <= trow[i] ? sc[i][j] * sl2 : -INFINITY;
+        mx = fmaxf(mx, x[j]);
+      }
+#pragma unroll
+      for (int off = 8; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+      const float mn = fmaxf(m[i], mx);
+      const float msub = mn == -INFINITY ? 0.f : mn;
+      const float alpha = exp2f(m[i] - msub);
+      float sum = 0.f;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float p = exp2f(x[j] - msub);
+        sum += p;
+        ps[(rg + 16 * i) * PS + cg + 16 * j] = p;
+      }
+#pragma unroll
+      for (int off = 8; off > 0; off >>= 1) sum += __shfl_xor(sum, off);
+      l[i] = l[i] * alpha + sum;
+      m[i] = mn;
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        o[i][c].x *= alpha;
+        o[i][c].y *= alpha;
+        o[i][c].z *= alpha;
+        o[i][c].w *= alpha;
+      }
+    }
+    __syncthreads();  // the probabilities of every row are in ps
+    const int kn = Tn - k0 < kF32Keys ? Tn - k0 : kF32Keys;
+    for (int k = 0; k < kn; ++k) {
+      float pv[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) pv[i] = ps[(rg + 16 * i) * PS + k];
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        const float4 lv = *(const float4*)&ls[k * QS + 4 * (cg + 16 * c)];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          o[i][c].x += pv[i] * lv.x;
+          o[i][c].y += pv[i] * lv.y;
+          o[i][c].z += pv[i] * lv.z;
+          o[i][c].w += pv[i] * lv.w;
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const long row = row0 + rg + 16 * i;
+    if (row >= TH) continue;
+    const float inv = 1.f / l[i];
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+      *(float4*)&o_lat[((size_t)b * TH + row) * R + 4 * (cg + 16 * c)] =
+          float4{o[i][c].x * inv, o[i][c].y * inv, o[i][c].z * inv, o[i][c].w * inv};
+  }
+}
+
+template <int R, typename T>
+static hipError_t attend_f32_tiled_launch(const float* q_lat, const T* lat, float* o_lat, int B, int Tn, int H,
+                                          float sl2, hipStream_t st) {
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute((const void*)attend_f32_tiled<R, T>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)attend_f32_lds_bytes<R>());
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  const long TH = (long)Tn * H;
+  hipLaunchKernelGGL((attend_f32_tiled<R, T>), dim3((unsigned)((TH + kF32Rows - 1) / kF32Rows), B), dim3(256),
+                     attend_f32_lds_bytes<R>(), st, q_lat, lat, o_lat, Tn, H, sl2);
+  return hipGetLastError();
+}
+
 // out[row, e] = sum_rho o_lat[row, rho] * W_uv[rho, h, e].  One block per row.
 template <typename T>
 __global__ void up_simt(const float* __restrict__ o_lat, const T* __restrict__ wv,
@@ -138,41 +304,44 @@ __global__ void up_simt(const float* __restrict__ o_lat, const T* __restrict__ w
   }
 }
 
-// C[M, N] = A[M, K] B[K, N], row-major, float32 accumulation; 64x64 tiles,
-// 16x16 threads with 4x4 outputs each, K staged through LDS 16 at a time.
-template <typename T>
+// C[M, N] = A[M, K] B[K, N], row-major, float32 accumulation; tiles of
+// 16 TS x 16 TS, 16x16 threads with TS x TS outputs each, K staged through
+// LDS 16 at a time.  TS = 4 (64x64 tiles), or TS = 2 (32x32) when the
+// 64x64 grid would leave compute units idle.
+template <typename T, int TS>
 __global__ void gemm_simt(const T* __restrict__ A, const T* __restrict__ Bm, T* __restrict__ C,
                           int M, int K, int N) {
-  __shared__ float As[16][65];
-  __shared__ float Bs[16][65];
+  constexpr int TW = 16 * TS;  // tile width
+  __shared__ float As[16][TW + 1];
+  __shared__ float Bs[16][TW + 1];
   const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
-  const int row0 = blockIdx.y * 64, col0 = blockIdx.x * 64;
-  float acc[4][4] = {};
+  const int row0 = blockIdx.y * TW, col0 = blockIdx.x * TW;
+  float acc[TS][TS] = {};
   for (int k0 = 0; k0 < K; k0 += 16) {
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < 16 * TW / 256; ++i) {  // both 16 x TW tiles, 256 elements at a time
       const int idx = tid + 256 * i;
       const int r = idx >> 4, k = idx & 15;
       As[k][r] = (row0 + r < M && k0 + k < K) ? io<T>::ld(A, (size_t)(row0 + r) * K + k0 + k) : 0.f;
-      const int kb = idx >> 6, c = idx & 63;
+      const int kb = idx / TW, c = idx % TW;
       Bs[kb][c] = (k0 + kb < K && col0 + c < N) ? io<T>::ld(Bm, (size_t)(k0 + kb) * N + col0 + c) : 0.f;
     }
     __syncthreads();
 #pragma unroll
     for (int k = 0; k < 16; ++k) {
-      float a[4], bb[4];
+      float a[TS], bb[TS];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) a[i] = As[k][ty + 16 * i];
+      for (int i = 0; i < TS; ++i) a[i] = As[k][ty + 16 * i];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) bb[j] = Bs[k][tx + 16 * j];
+      for (int j = 0; j < TS; ++j) bb[j] = Bs[k][tx + 16 * j];
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < TS; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] += a[i] * bb[j];
+        for (int j = 0; j < TS; ++j) acc[i][j] += a[i] * bb[j];
     }
     __syncthreads();
   }
-  for (int i = 0; i < 4; ++i)
-    for (int j = 0; j < 4; ++j) {
+  for (int i = 0; i < TS; ++i)
+    for (int j = 0; j < TS; ++j) {
       const int r = row0 + ty + 16 * i, c = col0 + tx + 16 * j;
       if (r < M && c < N) io<T>::st(C, (size_t)r * N + c, acc[i][j]);
     }
@@ -189,7 +358,13 @@ static hipError_t prefill_simt_t(const T* q, const T* lat, const T* wk, const T*
     ProfScope ps("absorb_simt", st);
     hipLaunchKernelGGL(absorb_simt<T>, dim3(rows), dim3(256), 0, st, q, wk, q_lat, H, d, r);
   }
-  {
+  if (!kmask && (r == 64 || r == 128 || r == 256)) {
+    ProfScope ps("attend_f32_tiled", st);
+    hipError_t e = r == 64    ? attend_f32_tiled_launch<64, T>(q_lat, lat, o_lat, B, T_, H, sl2, st)
+                   : r == 128 ? attend_f32_tiled_launch<128, T>(q_lat, lat, o_lat, B, T_, H, sl2, st)
+                              : attend_f32_tiled_launch<256, T>(q_lat, lat, o_lat, B, T_, H, sl2, st);
+    if (e != hipSuccess) return e;
+  } else {
     ProfScope ps("attend_simt", st);
     hipLaunchKernelGGL((attend_simt<T, false>), dim3((rows + 3) / 4), dim3(256), 0, st, q_lat, lat, nullptr,
                        (const int32_t*)nullptr, kmask, o_lat, T_, H, r, sl2, rows);
@@ -291,19 +466,24 @@ size_t decode_simt_workspace(int B, int Tmax, int H, int d, int r) {
 
 hipError_t down_proj(bool bf16, const void* hidden, const void* w_down, void* latent, int M, int D,
                      int r, hipStream_t st) {
-  const dim3 grid((r + 63) / 64, (M + 63) / 64);
-  if (bf16)
-    {
-      ProfScope ps("gemm_simt", st);
-      hipLaunchKernelGGL(gemm_simt<uint16_t>, grid, dim3(256), 0, st, (const uint16_t*)hidden,
+  ProfScope ps("gemm_simt", st);
+  const bool small = (long)((r + 63) / 64) * ((M + 63) / 64) < 512;  // 64x64 tiles would not fill the chip
+  const dim3 grid = small ? dim3((r + 31) / 32, (M + 31) / 32) : dim3((r + 63) / 64, (M + 63) / 64);
+  if (bf16) {
+    if (small)
+      hipLaunchKernelGGL((gemm_simt<uint16_t, 2>), grid, dim3(256), 0, st, (const uint16_t*)hidden,
                          (const uint16_t*)w_down, (uint16_t*)latent, M, D, r);
-    }
-  else
-    {
-      ProfScope ps("gemm_simt", st);
-      hipLaunchKernelGGL(gemm_simt<float>, grid, dim3(256), 0, st, (const float*)hidden,
+    else
+      hipLaunchKernelGGL((gemm_simt<uint16_t, 4>), grid, dim3(256), 0, st, (const uint16_t*)hidden,
+                         (const uint16_t*)w_down, (uint16_t*)latent, M, D, r);
+  } else {
+    if (small)
+      hipLaunchKernelGGL((gemm_simt<float, 2>), grid, dim3(256), 0, st, (const float*)hidden,
                          (const float*)w_down, (float*)latent, M, D, r);
-    }
+    else
+      hipLaunchKernelGGL((gemm_simt<float, 4>), grid, dim3(256), 0, st, (const float*)hidden,
+                         (const float*)w_down, (float*)latent, M, D, r);
+  }
   return hipGetLastError();
 }
 

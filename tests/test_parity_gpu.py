@@ -62,6 +62,10 @@ SMALL = [
     ("fp32_small", dict(T=129, r=512, d=128, H=2)),            # float32 at the wide latent
     ("bf16_prefill", dict(B=1, T=70, H=4, d=256)),             # d = 256: absorption in two rank halves
     ("bf16_prefill", dict(B=2, T=40, H=8, d=32, r=128)),       # d = 32
+    ("fp32_small", dict(B=2, T=100, H=3, d=16, r=64)),         # float32 tiled kernel, r = 64, ragged row blocks
+    ("fp32_small", dict(B=1, T=70, H=5, d=32, r=256)),         # float32 tiled kernel, r = 256
+    ("fp32_small", dict(B=1, T=300, H=1, d=32, r=128)),        # float32 tiled kernel, five key tiles
+    ("bf16_prefill", dict(B=2, T=90, H=4, d=16, r=64)),        # bf16 storage through the float32 tiled kernel
 ]
 
 
