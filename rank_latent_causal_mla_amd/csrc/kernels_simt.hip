@@ -21,23 +21,6 @@ __device__ __forceinline__ float wave_sum(float x) {
   return x;
 }
 
-// q_lat[row, rho] = sum_e q[row, e] * W_uk[rho, h, e], row = n*H + h.  One block per row.
-template <typename T>
-__global__ void absorb_simt(const T* __restrict__ q, const T* __restrict__ wk,
-                            float* __restrict__ q_lat, int H, int d, int R) {
-  __shared__ float qs[256];
-  const size_t row = blockIdx.x;
-  const int h = (int)(row % H);
-  for (int e = threadIdx.x; e < d; e += blockDim.x) qs[e] = io<T>::ld(q, row * d + e);
-  __syncthreads();
-  for (int rho = threadIdx.x; rho < R; rho += blockDim.x) {
-    const T* w = wk + ((size_t)rho * H + h) * d;
-    float acc = 0.f;
-    for (int e = 0; e < d; ++e) acc += qs[e] * io<T>::ld(w, e);
-    q_lat[row * R + rho] = acc;
-  }
-}
-
 // Streaming-softmax attention of one query row per wave over the latents.
 // Prefill: row = (b*T + t)*H + h attends keys 0..t of batch b; with kmask
 //          [B, T] bytes, only the keys s whose kmask[b, s] is nonzero (a masked
@@ -288,42 +271,35 @@ static hipError_t attend_f32_tiled_launch(const float* q_lat, const T* lat, floa
   return hipGetLastError();
 }
 
-// out[row, e] = sum_rho o_lat[row, rho] * W_uv[rho, h, e].  One block per row.
-template <typename T>
-__global__ void up_simt(const float* __restrict__ o_lat, const T* __restrict__ wv,
-                        T* __restrict__ out, int H, int d, int R) {
-  __shared__ float os[1024];
-  const size_t row = blockIdx.x;
-  const int h = (int)(row % H);
-  for (int rho = threadIdx.x; rho < R; rho += blockDim.x) os[rho] = o_lat[row * R + rho];
-  __syncthreads();
-  for (int e = threadIdx.x; e < d; e += blockDim.x) {
-    float acc = 0.f;
-    for (int rho = 0; rho < R; ++rho) acc += os[rho] * io<T>::ld(wv, ((size_t)rho * H + h) * d + e);
-    io<T>::st(out, row * d + e, acc);
-  }
-}
-
-// C[M, N] = A[M, K] B[K, N], row-major, float32 accumulation; tiles of
-// 16 TS x 16 TS, 16x16 threads with TS x TS outputs each, K staged through
-// LDS 16 at a time.  TS = 4 (64x64 tiles), or TS = 2 (32x32) when the
-// 64x64 grid would leave compute units idle.
-template <typename T, int TS>
-__global__ void gemm_simt(const T* __restrict__ A, const T* __restrict__ Bm, T* __restrict__ C,
-                          int M, int K, int N) {
+// Strided batched GEMM in float32: for batch z (blockIdx.z),
+//   C[m*ldc + n] = sum_k A[m*lda + k] * B[k*ldbk + n*ldbn]
+// with A, B, C offset by z*a_bs, z*b_bs, z*c_bs elements.  Tiles of 16 TS x
+// 16 TS, 16x16 threads with TS x TS outputs each, k staged through LDS 16
+// at a time; B is read along k when ldbk == 1 (k contiguous), else along n.
+// TS = 4 (64x64 tiles) or 2 (32x32) when 64x64 tiles would leave compute
+// units idle.
+template <typename TA, typename TB, typename TC, int TS>
+__global__ __launch_bounds__(256) void gemm_strided(const TA* __restrict__ A, const TB* __restrict__ Bm,
+                                                    TC* __restrict__ C, int M, int K, int N, long lda, long ldbk,
+                                                    long ldbn, long ldc, long a_bs, long b_bs, long c_bs) {
   constexpr int TW = 16 * TS;  // tile width
   __shared__ float As[16][TW + 1];
   __shared__ float Bs[16][TW + 1];
+  A += blockIdx.z * a_bs;
+  Bm += blockIdx.z * b_bs;
+  C += blockIdx.z * c_bs;
   const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
   const int row0 = blockIdx.y * TW, col0 = blockIdx.x * TW;
+  const bool bk = ldbk == 1;
   float acc[TS][TS] = {};
   for (int k0 = 0; k0 < K; k0 += 16) {
     for (int i = 0; i < 16 * TW / 256; ++i) {  // both 16 x TW tiles, 256 elements at a time
       const int idx = tid + 256 * i;
       const int r = idx >> 4, k = idx & 15;
-      As[k][r] = (row0 + r < M && k0 + k < K) ? io<T>::ld(A, (size_t)(row0 + r) * K + k0 + k) : 0.f;
-      const int kb = idx / TW, c = idx % TW;
-      Bs[kb][c] = (k0 + kb < K && col0 + c < N) ? io<T>::ld(Bm, (size_t)(k0 + kb) * N + col0 + c) : 0.f;
+      As[k][r] = (row0 + r < M && k0 + k < K) ? io<TA>::ld(A, (size_t)(row0 + r) * lda + k0 + k) : 0.f;
+      const int kb = bk ? idx & 15 : idx / TW, c = bk ? idx >> 4 : idx % TW;
+      Bs[kb][c] = (k0 + kb < K && col0 + c < N) ? io<TB>::ld(Bm, (size_t)(k0 + kb) * ldbk + (size_t)(col0 + c) * ldbn)
+                                                  : 0.f;
     }
     __syncthreads();
 #pragma unroll
@@ -343,8 +319,39 @@ __global__ void gemm_simt(const T* __restrict__ A, const T* __restrict__ Bm, T* 
   for (int i = 0; i < TS; ++i)
     for (int j = 0; j < TS; ++j) {
       const int r = row0 + ty + 16 * i, c = col0 + tx + 16 * j;
-      if (r < M && c < N) io<T>::st(C, (size_t)r * N + c, acc[i][j]);
+      if (r < M && c < N) io<TC>::st(C, (size_t)r * ldc + c, acc[i][j]);
     }
+}
+
+template <typename TA, typename TB, typename TC>
+static hipError_t gemm_launch(const TA* A, const TB* Bm, TC* C, int M, int K, int N, long lda, long ldbk, long ldbn,
+                              long ldc, int batches, long a_bs, long b_bs, long c_bs, hipStream_t st) {
+  const long tiles64 = (long)((N + 63) / 64) * ((M + 63) / 64) * batches;
+  if (tiles64 < 512) {  // 64x64 tiles would not fill the chip
+    hipLaunchKernelGGL((gemm_strided<TA, TB, TC, 2>), dim3((N + 31) / 32, (M + 31) / 32, batches), dim3(256), 0, st,
+                       A, Bm, C, M, K, N, lda, ldbk, ldbn, ldc, a_bs, b_bs, c_bs);
+  } else {
+    hipLaunchKernelGGL((gemm_strided<TA, TB, TC, 4>), dim3((N + 63) / 64, (M + 63) / 64, batches), dim3(256), 0, st,
+                       A, Bm, C, M, K, N, lda, ldbk, ldbn, ldc, a_bs, b_bs, c_bs);
+  }
+  return hipGetLastError();
+}
+
+// Absorption, every head at once: q_lat[n, h, rho] = sum_e q[n, h, e] W_uk[rho, h, e]
+// (n < Ntok; q_lat float32 [Ntok][H][R]).
+template <typename T>
+static hipError_t absorb_gemm(const T* q, const T* wk, float* q_lat, long Ntok, int H, int d, int R, hipStream_t st) {
+  ProfScope ps("absorb_simt", st);
+  return gemm_launch<T, T, float>(q, wk, q_lat, (int)Ntok, d, R, (long)H * d, 1, (long)H * d, (long)H * R, H, d, d,
+                                  R, st);
+}
+
+// Up-projection, every head at once: out[n, h, e] = sum_rho o_lat[n, h, rho] W_uv[rho, h, e].
+template <typename T>
+static hipError_t up_gemm(const float* o_lat, const T* wv, T* out, long Ntok, int H, int d, int R, hipStream_t st) {
+  ProfScope ps("up_simt", st);
+  return gemm_launch<float, T, T>(o_lat, wv, out, (int)Ntok, R, d, (long)H * R, (long)H * d, 1, (long)H * d, H, R, d,
+                                  d, st);
 }
 
 template <typename T>
@@ -355,8 +362,8 @@ static hipError_t prefill_simt_t(const T* q, const T* lat, const T* wk, const T*
   float* q_lat = (float*)ws;
   float* o_lat = q_lat + (size_t)rows * r;
   {
-    ProfScope ps("absorb_simt", st);
-    hipLaunchKernelGGL(absorb_simt<T>, dim3(rows), dim3(256), 0, st, q, wk, q_lat, H, d, r);
+    hipError_t e = absorb_gemm<T>(q, wk, q_lat, rows / H, H, d, r, st);
+    if (e != hipSuccess) return e;
   }
   if (!kmask && (r == 64 || r == 128 || r == 256)) {
     ProfScope ps("attend_f32_tiled", st);
@@ -370,8 +377,8 @@ static hipError_t prefill_simt_t(const T* q, const T* lat, const T* wk, const T*
                        (const int32_t*)nullptr, kmask, o_lat, T_, H, r, sl2, rows);
   }
   {
-    ProfScope ps("up_simt", st);
-    hipLaunchKernelGGL(up_simt<T>, dim3(rows), dim3(256), 0, st, o_lat, wv, out, H, d, r);
+    hipError_t e = up_gemm<T>(o_lat, wv, out, rows / H, H, d, r, st);
+    if (e != hipSuccess) return e;
   }
   return hipGetLastError();
 }
@@ -384,8 +391,8 @@ static hipError_t decode_simt_t(const T* q, const T* lat, const int32_t* lens, c
   float* q_lat = (float*)ws;
   float* o_lat = q_lat + (size_t)rows * r;
   {
-    ProfScope ps("absorb_simt", st);
-    hipLaunchKernelGGL(absorb_simt<T>, dim3(rows), dim3(256), 0, st, q, wk, q_lat, H, d, r);
+    hipError_t e = absorb_gemm<T>(q, wk, q_lat, rows / H, H, d, r, st);
+    if (e != hipSuccess) return e;
   }
   {
     ProfScope ps("attend_simt", st);
@@ -393,8 +400,8 @@ static hipError_t decode_simt_t(const T* q, const T* lat, const int32_t* lens, c
                        lens, cu, (const uint8_t*)nullptr, o_lat, Tmax, H, r, sl2, rows);
   }
   {
-    ProfScope ps("up_simt", st);
-    hipLaunchKernelGGL(up_simt<T>, dim3(rows), dim3(256), 0, st, o_lat, wv, out, H, d, r);
+    hipError_t e = up_gemm<T>(o_lat, wv, out, rows / H, H, d, r, st);
+    if (e != hipSuccess) return e;
   }
   return hipGetLastError();
 }
@@ -467,24 +474,11 @@ size_t decode_simt_workspace(int B, int Tmax, int H, int d, int r) {
 hipError_t down_proj(bool bf16, const void* hidden, const void* w_down, void* latent, int M, int D,
                      int r, hipStream_t st) {
   ProfScope ps("gemm_simt", st);
-  const bool small = (long)((r + 63) / 64) * ((M + 63) / 64) < 512;  // 64x64 tiles would not fill the chip
-  const dim3 grid = small ? dim3((r + 31) / 32, (M + 31) / 32) : dim3((r + 63) / 64, (M + 63) / 64);
-  if (bf16) {
-    if (small)
-      hipLaunchKernelGGL((gemm_simt<uint16_t, 2>), grid, dim3(256), 0, st, (const uint16_t*)hidden,
-                         (const uint16_t*)w_down, (uint16_t*)latent, M, D, r);
-    else
-      hipLaunchKernelGGL((gemm_simt<uint16_t, 4>), grid, dim3(256), 0, st, (const uint16_t*)hidden,
-                         (const uint16_t*)w_down, (uint16_t*)latent, M, D, r);
-  } else {
-    if (small)
-      hipLaunchKernelGGL((gemm_simt<float, 2>), grid, dim3(256), 0, st, (const float*)hidden,
-                         (const float*)w_down, (float*)latent, M, D, r);
-    else
-      hipLaunchKernelGGL((gemm_simt<float, 4>), grid, dim3(256), 0, st, (const float*)hidden,
-                         (const float*)w_down, (float*)latent, M, D, r);
-  }
-  return hipGetLastError();
+  if (bf16)
+    return gemm_launch<uint16_t, uint16_t, uint16_t>((const uint16_t*)hidden, (const uint16_t*)w_down,
+                                                     (uint16_t*)latent, M, D, r, D, r, 1, r, 1, 0, 0, 0, st);
+  return gemm_launch<float, float, float>((const float*)hidden, (const float*)w_down, (float*)latent, M, D, r, D, r,
+                                          1, r, 1, 0, 0, 0, st);
 }
 
 }  // namespace mla
