@@ -379,7 +379,7 @@ def main(argv=None):
                      dataclasses.replace(synth.CONFIGS["bf16_prefill"], name="bf16_prefill_down1024", D=1024)):
             fms, fkt = bench_full(fcfg, args.steps, args.warmup)
             fw = prefill_flops(fcfg)
-            down = fkt.get("down_bf16") or fkt.get("gemm_simt")
+            down = fkt.get("down_bf16") or fkt.get("down_f32")
             if fcfg.dtype == "bf16":
                 dom, dom_flops, bound, peak = fkt.get("flash_latent_bf16"), fw["attn"], "mfma", PEAK_BF16_TFLOPS
                 dom_name = "flash_latent_bf16"

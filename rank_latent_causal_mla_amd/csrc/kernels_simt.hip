@@ -341,7 +341,7 @@ static hipError_t gemm_launch(const TA* A, const TB* Bm, TC* C, int M, int K, in
 // (n < Ntok; q_lat float32 [Ntok][H][R]).
 template <typename T>
 static hipError_t absorb_gemm(const T* q, const T* wk, float* q_lat, long Ntok, int H, int d, int R, hipStream_t st) {
-  ProfScope ps("absorb_simt", st);
+  ProfScope ps("absorb_f32", st);
   return gemm_launch<T, T, float>(q, wk, q_lat, (int)Ntok, d, R, (long)H * d, 1, (long)H * d, (long)H * R, H, d, d,
                                   R, st);
 }
@@ -349,7 +349,7 @@ static hipError_t absorb_gemm(const T* q, const T* wk, float* q_lat, long Ntok, 
 // Up-projection, every head at once: out[n, h, e] = sum_rho o_lat[n, h, rho] W_uv[rho, h, e].
 template <typename T>
 static hipError_t up_gemm(const float* o_lat, const T* wv, T* out, long Ntok, int H, int d, int R, hipStream_t st) {
-  ProfScope ps("up_simt", st);
+  ProfScope ps("up_f32", st);
   return gemm_launch<float, T, T>(o_lat, wv, out, (int)Ntok, R, d, (long)H * R, (long)H * d, 1, (long)H * d, H, R, d,
                                   d, st);
 }
@@ -473,7 +473,7 @@ size_t decode_simt_workspace(int B, int Tmax, int H, int d, int r) {
 
 hipError_t down_proj(bool bf16, const void* hidden, const void* w_down, void* latent, int M, int D,
                      int r, hipStream_t st) {
-  ProfScope ps("gemm_simt", st);
+  ProfScope ps("down_f32", st);
   if (bf16)
     return gemm_launch<uint16_t, uint16_t, uint16_t>((const uint16_t*)hidden, (const uint16_t*)w_down,
                                                      (uint16_t*)latent, M, D, r, D, r, 1, r, 1, 0, 0, 0, st);
