@@ -276,3 +276,18 @@ def test_first_row_is_v0():
     wv = synth.bf16_bits_to_f32(inp["w_up_v"]).astype(np.float64)
     v0 = np.einsum("br,rhe->bhe", lat[:, 0], wv)
     compare(to_f64(out[:, 0]), v0, "bf16", "row 0 = v_0")
+
+
+def test_decode_many_short_sequences():
+    """300 sequences of 1..40 cached latents: every chunk of the balanced split
+    holds many sequence segments (one partial state each), and many
+    sequences sit in a single chunk."""
+    import synth as _s
+    cfg = cfg_like("bf16_decode", B=300, T=40, H=32)
+    inp = synth.make_inputs(cfg)
+    lens = (_s.randint(cfg.seed, 11, cfg.B, 1, 40)).tolist()
+    print(f"many short decode sequences, sum L = {sum(lens)}", flush=True)
+    out = run_decode(cfg, inp, lens, pad_nan=True)
+    ref = oracle.decode(inp["q"], inp["kv_latent"], lens, inp["w_up_k"], inp["w_up_v"], cfg.scale)
+    err = compare(to_f64(out), ref, cfg.dtype, "decode, many short sequences")
+    print(f"max abs err {err:.3e}")
