@@ -134,6 +134,23 @@ mla_status mla_latent_attn_fwd_unabsorbed(const void* q, const void* kv_latent, 
                                           int r, float scale, mla_dtype dt, void* workspace,
                                           size_t workspace_bytes, void* stream);
 
+/* The form mla_latent_attn_fwd_auto takes for this shape: 1 for the
+ * unabsorbed form (bf16, a shape mla_latent_attn_fwd_unabsorbed covers, and
+ * r > d, where materialising k and v takes r/d times fewer matrix
+ * operations), 0 for the absorbed form otherwise. */
+int mla_latent_attn_auto_form(int B, int T, int H, int d, int r, mla_dtype dt);
+
+/* Bytes of workspace mla_latent_attn_fwd_auto needs (that of the form it takes). */
+size_t mla_latent_attn_auto_workspace_size(int B, int T, int H, int d, int r, mla_dtype dt);
+
+/* The causal prefill of mla_latent_attn_fwd (same arguments, same result up
+ * to rounding) in the form mla_latent_attn_auto_form picks for the shape:
+ * the absorbed form of mla_latent_attn_fwd or the unabsorbed form of
+ * mla_latent_attn_fwd_unabsorbed, whose result it returns bit for bit. */
+mla_status mla_latent_attn_fwd_auto(const void* q, const void* kv_latent, const void* w_up_k, const void* w_up_v,
+                                    void* out, int B, int T, int H, int d, int r, float scale, mla_dtype dt,
+                                    void* workspace, size_t workspace_bytes, void* stream);
+
 /* Bytes of workspace mla_decode_fwd needs for this shape (0 on bad sizes). */
 size_t mla_decode_workspace_size(int B, int Tmax, int H, int d, int r, mla_dtype dt);
 

@@ -21,6 +21,7 @@ MLA_DTYPE_F32, MLA_DTYPE_BF16 = 0, 1
 EXPORTED = ("mla_down_proj", "mla_latent_attn_workspace_size", "mla_latent_attn_fwd",
             "mla_latent_attn_masked_workspace_size", "mla_latent_attn_fwd_masked",
             "mla_latent_attn_full_workspace_size", "mla_latent_attn_fwd_full",
+            "mla_latent_attn_auto_form", "mla_latent_attn_auto_workspace_size", "mla_latent_attn_fwd_auto",
             "mla_latent_attn_unabsorbed_workspace_size", "mla_latent_attn_fwd_unabsorbed",
             "mla_decode_workspace_size", "mla_decode_fwd", "mla_decode_varlen_workspace_size",
             "mla_decode_varlen_fwd", "mla_kv_append", "mla_profile_enable", "mla_profile_collect",
@@ -59,6 +60,12 @@ def load():
     lib.mla_latent_attn_workspace_size.argtypes = [i32] * 6
     lib.mla_latent_attn_fwd.restype = i32
     lib.mla_latent_attn_fwd.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, i32, vp, sz, vp]
+    lib.mla_latent_attn_auto_form.restype = i32
+    lib.mla_latent_attn_auto_form.argtypes = [i32] * 6
+    lib.mla_latent_attn_auto_workspace_size.restype = sz
+    lib.mla_latent_attn_auto_workspace_size.argtypes = [i32] * 6
+    lib.mla_latent_attn_fwd_auto.restype = i32
+    lib.mla_latent_attn_fwd_auto.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, i32, vp, sz, vp]
     lib.mla_latent_attn_full_workspace_size.restype = sz
     lib.mla_latent_attn_full_workspace_size.argtypes = [i32] * 7
     lib.mla_latent_attn_fwd_full.restype = i32
@@ -117,6 +124,20 @@ def mla_down_proj_raw(hidden, w_down, kv_latent, B, T, D, r, dt, stream=0):
 
 def mla_latent_attn_workspace_size(B, T, H, d, r, dt):
     return int(load().mla_latent_attn_workspace_size(B, T, H, d, r, dt))
+
+
+def mla_latent_attn_auto_form(B, T, H, d, r, dt):
+    """1 when mla_latent_attn_fwd_auto takes the unabsorbed form for this shape, else 0."""
+    return int(load().mla_latent_attn_auto_form(B, T, H, d, r, dt))
+
+
+def mla_latent_attn_auto_workspace_size(B, T, H, d, r, dt):
+    return int(load().mla_latent_attn_auto_workspace_size(B, T, H, d, r, dt))
+
+
+def mla_latent_attn_fwd_auto_raw(q, kv_latent, w_up_k, w_up_v, out, B, T, H, d, r, scale, dt, ws, ws_bytes, stream=0):
+    return load().mla_latent_attn_fwd_auto(q, kv_latent, w_up_k, w_up_v, out, B, T, H, d, r, scale, dt, ws, ws_bytes,
+                                           stream)
 
 
 def mla_latent_attn_full_workspace_size(B, T, D, H, d, r, dt):
@@ -289,6 +310,28 @@ def mla_latent_attn_fwd_masked(q, kv_latent, key_mask, w_up_k, w_up_v, out=None,
                                           w_up_v.data_ptr(), out.data_ptr(), B, T, H, d, r, float(scale), dt,
                                           workspace.data_ptr(), workspace.numel() * workspace.element_size(),
                                           _stream(stream)))
+    return out
+
+
+def mla_latent_attn_fwd_auto(q, kv_latent, w_up_k, w_up_v, out=None, scale=None, workspace=None, stream=None):
+    """The causal prefill in the form the library picks for the shape (mla_latent_attn_auto_form)."""
+    import torch
+    _dev(q, kv_latent, w_up_k, w_up_v)
+    B, T, H, d = q.shape
+    r = kv_latent.shape[-1]
+    dt = _dt(q)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    _shaped(out, q.shape, q.dtype, "out")
+    nbytes = mla_latent_attn_auto_workspace_size(B, T, H, d, r, dt)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    _dev(out, workspace)
+    _check(mla_latent_attn_fwd_auto_raw(q.data_ptr(), kv_latent.data_ptr(), w_up_k.data_ptr(), w_up_v.data_ptr(),
+                                        out.data_ptr(), B, T, H, d, r, float(scale), dt, workspace.data_ptr(),
+                                        workspace.numel() * workspace.element_size(), _stream(stream)))
     return out
 
 

@@ -250,6 +250,28 @@ mla_status mla_latent_attn_fwd_unabsorbed(const void* q, const void* kv_latent, 
                   "unabsorbed prefill launch");
 }
 
+int mla_latent_attn_auto_form(int B, int T, int H, int d, int r, mla_dtype dt) {
+  (void)B;
+  (void)T;
+  (void)H;
+  return dt == MLA_DTYPE_BF16 && mla::unabsorbed_supported(d, r) && r > d ? 1 : 0;
+}
+
+size_t mla_latent_attn_auto_workspace_size(int B, int T, int H, int d, int r, mla_dtype dt) {
+  return mla_latent_attn_auto_form(B, T, H, d, r, dt) ? mla_latent_attn_unabsorbed_workspace_size(B, T, H, d, r, dt)
+                                                      : mla_latent_attn_workspace_size(B, T, H, d, r, dt);
+}
+
+mla_status mla_latent_attn_fwd_auto(const void* q, const void* kv_latent, const void* w_up_k, const void* w_up_v,
+                                    void* out, int B, int T, int H, int d, int r, float scale, mla_dtype dt,
+                                    void* workspace, size_t workspace_bytes, void* stream) {
+  if (mla_latent_attn_auto_form(B, T, H, d, r, dt))
+    return mla_latent_attn_fwd_unabsorbed(q, kv_latent, w_up_k, w_up_v, out, B, T, H, d, r, scale, dt, workspace,
+                                          workspace_bytes, stream);
+  return mla_latent_attn_fwd(q, kv_latent, w_up_k, w_up_v, out, B, T, H, d, r, scale, dt, workspace,
+                             workspace_bytes, stream);
+}
+
 size_t mla_decode_workspace_size(int B, int Tmax, int H, int d, int r, mla_dtype dt) {
   if (B < 1 || Tmax < 1 || H < 1 || d < 1 || r < 1) return 0;
   if (dt != MLA_DTYPE_F32 && dt != MLA_DTYPE_BF16) return 0;

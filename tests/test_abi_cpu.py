@@ -14,7 +14,7 @@ P = 1 << 20   # a 16-byte aligned fake address: never dereferenced on these path
 
 def declared_symbols():
     text = open(os.path.join(ROOT, "include", "mla.h")).read()
-    return sorted(set(re.findall(r"^\s*(?:mla_status|size_t|const char\*)\s+(mla_\w+)\s*\(", text, re.M)))
+    return sorted(set(re.findall(r"^\s*(?:mla_status|size_t|int|const char\*)\s+(mla_\w+)\s*\(", text, re.M)))
 
 
 def test_header_declares_the_abi():
@@ -251,3 +251,16 @@ def test_full_workspace_size():
     # the workspace test above must pass with the full requirement, not the attention one
     need = mla.mla_latent_attn_full_workspace_size(2, 64, 1024, 4, 128, 512, BF16)
     assert full(dt=BF16, d=128, r=512, D=1024, wsb=need - 1) == mla.MLA_ERR_WORKSPACE
+
+
+def test_auto_form_choice():
+    # unabsorbed where it is covered and r > d; absorbed otherwise
+    assert mla.mla_latent_attn_auto_form(2, 16384, 64, 128, 512, BF16) == 1
+    assert mla.mla_latent_attn_auto_form(8, 2048, 16, 128, 256, BF16) == 1
+    assert mla.mla_latent_attn_auto_form(8, 2048, 16, 128, 128, BF16) == 0     # r = d
+    assert mla.mla_latent_attn_auto_form(8, 2048, 16, 64, 512, BF16) == 0      # d not covered by the unabsorbed form
+    assert mla.mla_latent_attn_auto_form(4, 512, 8, 64, 128, F32) == 0         # float32
+    assert mla.mla_latent_attn_auto_workspace_size(2, 64, 4, 128, 512, BF16) == \
+        mla.mla_latent_attn_unabsorbed_workspace_size(2, 64, 4, 128, 512, BF16)
+    assert mla.mla_latent_attn_auto_workspace_size(2, 64, 4, 32, 32, F32) == \
+        mla.mla_latent_attn_workspace_size(2, 64, 4, 32, 32, F32)

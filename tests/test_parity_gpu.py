@@ -291,3 +291,21 @@ def test_decode_many_short_sequences():
     ref = oracle.decode(inp["q"], inp["kv_latent"], lens, inp["w_up_k"], inp["w_up_v"], cfg.scale)
     err = compare(to_f64(out), ref, cfg.dtype, "decode, many short sequences")
     print(f"max abs err {err:.3e}")
+
+
+@pytest.mark.parametrize("kw", [dict(B=2, T=100, H=4), dict(B=2, T=100, H=4, r=128), dict(B=1, T=70, H=2, d=64)])
+def test_auto_form_is_the_chosen_form_bitwise(kw):
+    """mla_latent_attn_fwd_auto returns exactly what the form it picks returns."""
+    import torch
+    cfg = cfg_like("bf16_prefill", **kw)
+    inp = synth.make_inputs(cfg)
+    dev = {k: to_device(v) for k, v in inp.items()}
+    args = (dev["q"], dev["kv_latent"], dev["w_up_k"], dev["w_up_v"])
+    got = mla.mla_latent_attn_fwd_auto(*args, scale=cfg.scale)
+    form = mla.mla_latent_attn_auto_form(cfg.B, cfg.T, cfg.H, cfg.d, cfg.r, mla.MLA_DTYPE_BF16)
+    ref = (mla.mla_latent_attn_fwd_unabsorbed if form else mla.mla_latent_attn_fwd)(*args, scale=cfg.scale)
+    torch.cuda.synchronize()
+    print(f"{cfg}: form {form}")
+    assert torch.equal(got.view(torch.int16), ref.view(torch.int16))
+    compare(to_f64(got), oracle.latent_attn(inp["q"], inp["kv_latent"], inp["w_up_k"], inp["w_up_v"], cfg.scale),
+            "bf16", "auto form")
