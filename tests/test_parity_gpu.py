@@ -91,7 +91,7 @@ def test_full_path_config():
 
 
 # ---------------------------------------------------------------- prefill at full size, sampled rows
-def sampled_prefill(cfg, heads, rows_per_head, seed=1, fwd=None):
+def sampled_prefill(cfg, heads, rows_per_head, seed=1, fwd=None, extra_rows=()):
     import torch
     inp = synth.make_inputs(cfg)
     print(f"full-size prefill {cfg.name} {'' if fwd is None else fwd.__name__}", flush=True)
@@ -100,7 +100,7 @@ def sampled_prefill(cfg, heads, rows_per_head, seed=1, fwd=None):
     assert torch.isfinite(out).all().item()
     rng = np.random.default_rng(seed)
     T = cfg.T
-    fixed = [0, 1, 31, 32, 33, 127, 128, 255, 256, T // 2, T - 2, T - 1]
+    fixed = [0, 1, 31, 32, 33, 127, 128, 255, 256, T // 2, T - 2, T - 1, *extra_rows]
     rb, rh, rt = [], [], []
     for (b, h) in heads:
         ts = sorted(set(fixed + list(rng.integers(0, T, rows_per_head))))
@@ -123,6 +123,18 @@ def test_bf16_prefill_full_size_sampled():
 
 def test_bf16_long_prefill_full_size_sampled():
     sampled_prefill(synth.CONFIGS["bf16_long_prefill"], heads=[(0, 0), (1, 63)], rows_per_head=12)
+
+
+def test_prefill_beyond_int32_offsets_sampled():
+    """B=4, T=16400, H=64, r=512: q_lat and o_lat hold 4*16400*64*512 > 2^31
+    elements, so the rows of batch 3 from t = 16336 on sit past every 32-bit
+    element offset.  Sampled rows on both sides of that line, in the last
+    batch and the others, against the oracle."""
+    cfg = cfg_like("bf16_long_prefill", B=4, T=16400)
+    assert cfg.B * cfg.T * cfg.H * cfg.r > 2 ** 31
+    first_past = 2 ** 31 // (cfg.H * cfg.r) - 3 * cfg.T   # first row of batch 3 past 2^31 elements
+    sampled_prefill(cfg, heads=[(3, 0), (3, 63), (3, 31), (0, 5), (2, 40)], rows_per_head=3,
+                    extra_rows=(first_past - 1, first_past, first_past + 1))
 
 
 # ---------------------------------------------------------------- unabsorbed prefill (k, v materialised)
