@@ -237,6 +237,43 @@ def test_decode_full_size_sampled():
     tight(out[rb, 0, rh], ref)
 
 
+def test_decode_beyond_int32_offsets():
+    """Padded cache [5][1,050,000][512] (5.4 GB): sequence 4 starts past 2^31
+    elements.  Every row past a length is NaN and must not be read.  Decode,
+    then one cache append per sequence and decode again, against the oracle
+    on three heads of every sequence."""
+    import torch
+    cfg = cfg_like("bf16_decode", B=5, T=1_050_000)
+    lens = np.array([1000, 3000, 33, 2048, 1500], np.int32)
+    assert (cfg.B - 1) * cfg.T * cfg.r > 2 ** 31
+    small = synth.make_inputs(dataclasses.replace(cfg, T=1))   # q and the weights do not depend on T
+    lat = np.zeros((cfg.B, int(lens.max()) + 1, cfg.r), np.uint16)
+    print(f"decode past 32-bit offsets {cfg} lens={lens.tolist()}", flush=True)
+    cache = torch.full((cfg.B, cfg.T, cfg.r), float("nan"), dtype=torch.bfloat16, device="cuda")
+    for b, L in enumerate(lens):
+        lat[b, :L + 1] = synth.make_rows(cfg, "kv_latent", b, 0, int(L) + 1).reshape(int(L) + 1, cfg.r)
+        cache[b, :L] = to_device(lat[b, :L])
+    dev = {k: to_device(v) for k, v in small.items() if k not in ("seq_lens", "kv_latent")}
+    dlens = torch.from_numpy(lens).cuda()
+    rb = np.repeat(np.arange(cfg.B), 3)
+    rh = np.tile(np.array([0, 13, cfg.H - 1]), cfg.B)
+    for step in range(2):
+        out = mla.mla_decode_fwd(dev["q"], cache, dlens, dev["w_up_k"], dev["w_up_v"], scale=cfg.scale)
+        torch.cuda.synchronize()
+        L = lens + step
+        ref = oracle.attend_rows(small["q"][rb, 0, rh], rb, rh, L[rb], lat, small["w_up_k"], small["w_up_v"],
+                                 cfg.scale)
+        got = to_f64(out)[rb, 0, rh]
+        err = compare(got, ref, "bf16", f"decode past 32-bit offsets, step {step}")
+        print(f"step {step}: max abs err {err:.3e}")
+        tight(got, ref)
+        if step == 0:
+            new = np.ascontiguousarray(lat[np.arange(cfg.B), lens])
+            mla.mla_kv_append(cache, dlens, to_device(new))
+            torch.cuda.synchronize()
+            assert np.array_equal(dlens.cpu().numpy(), lens + 1)
+
+
 def test_decode_equals_last_prefill_row():
     import torch
     cfg = cfg_like("bf16_prefill", B=2, T=200, H=16)
