@@ -358,3 +358,35 @@ def test_auto_form_is_the_chosen_form_bitwise(kw):
     assert torch.equal(got.view(torch.int16), ref.view(torch.int16))
     compare(to_f64(got), oracle.latent_attn(inp["q"], inp["kv_latent"], inp["w_up_k"], inp["w_up_v"], cfg.scale),
             "bf16", "auto form")
+
+
+def test_calls_run_on_the_callers_stream():
+    """Each call is enqueued on the caller's stream: its inputs are written on
+    a side stream behind a long chain of products, so a call launched on any
+    other stream would read them early.  Prefill, masked prefill and decode
+    on the side stream equal the same calls on the default stream bit for bit."""
+    import torch
+    cfg = cfg_like("bf16_prefill", B=2, T=300, H=8)
+    inp = synth.make_inputs(cfg)
+    dev = {k: to_device(v) for k, v in inp.items()}
+    mask = torch.from_numpy(synth.make_key_mask(cfg, p_hole=0.2, lead=3)).cuda()
+    lens = torch.tensor([300, 123], dtype=torch.int32, device="cuda")
+    qd = dev["q"][:, -1:].contiguous()
+    args = (dev["w_up_k"], dev["w_up_v"])
+    ref = [mla.mla_latent_attn_fwd(dev["q"], dev["kv_latent"], *args, scale=cfg.scale),
+           mla.mla_latent_attn_fwd_masked(dev["q"], dev["kv_latent"], mask, *args, scale=cfg.scale),
+           mla.mla_decode_fwd(qd, dev["kv_latent"], lens, *args, scale=cfg.scale)]
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    x = torch.randn(2048, 2048, device="cuda")
+    with torch.cuda.stream(side):
+        for _ in range(40):
+            x = torch.tanh(torch.mm(x, x))
+        q = torch.zeros_like(dev["q"]) + x[0, 0] * 0 + dev["q"]   # written only after the chain
+        lat = torch.zeros_like(dev["kv_latent"]) + x[0, 1] * 0 + dev["kv_latent"]
+        got = [mla.mla_latent_attn_fwd(q, lat, *args, scale=cfg.scale),
+               mla.mla_latent_attn_fwd_masked(q, lat, mask, *args, scale=cfg.scale),
+               mla.mla_decode_fwd(q[:, -1:].contiguous(), lat, lens, *args, scale=cfg.scale)]
+    torch.cuda.synchronize()
+    for a, b in zip(got, ref):
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16))
