@@ -18,7 +18,10 @@
  *     tensors of one call share the dtype `dt` (float32 or bf16); seq_lens is
  *     int32.  Float pointers must be 16-byte aligned.
  *   - `stream` is a hipStream_t (NULL = the default stream).  Work is only
- *     enqueued on it; no call synchronises the host.
+ *     enqueued on it; no call synchronises the host.  Calls enqueue kernel
+ *     launches only (no memset, copy or allocation), so a stream capture
+ *     may record them into a HIP graph for replay; the first call of each
+ *     kernel shape sets its LDS attribute and should precede the capture.
  *   - Arguments are checked before anything is enqueued.  A null pointer,
  *     a non-positive size or misalignment returns MLA_ERR_INVALID_ARGUMENT;
  *     a shape the kernels do not cover returns MLA_ERR_UNSUPPORTED; a
