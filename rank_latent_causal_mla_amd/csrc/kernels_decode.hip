@@ -98,44 +98,48 @@ void decode_split(const uint16_t* __restrict__ q_lat, const uint16_t* __restrict
   auto seg_more = [&](int b) { return b < B && __builtin_amdgcn_readfirstlane(S[b]) < x1; };
   const int k_first = x0 - __builtin_amdgcn_readfirstlane(S[b_first]);
 
-  // The chunk as one stream of 32-key tiles, segment after segment; the copy
-  // cursor runs three tiles ahead of the compute cursor, across segments.
+  // The chunk as one stream of ring items, segment after segment: the query
+  // block of a segment's sequence (its 32 heads' q_lat rows, the same size as
+  // a tile and copied the same way), then the segment's 32-key tiles.  The
+  // copy cursor runs three items ahead of the compute cursor, across
+  // segments.  The queries travel through the ring because a plain load of
+  // them would be counted with the copies in flight, and waiting for it
+  // would drain the stream at every segment start.
+  const int qrows = H - hg * 32 < 32 ? H - hg * 32 : 32;  // heads of this group (rows past it repeat the last)
   int db = b_first, dk = k_first, dend = seg_end(b_first);
+  bool dq = true;  // the next item is the query block of sequence db
   bool ddone = false;
   int issued = 0;
   auto copy_next = [&]() {
-    const int rb = __builtin_amdgcn_readfirstlane(RB[db]);  // first cache row of sequence db
-    dma_tile32<R>(lat + (size_t)rb * R, dk, dend, lds0 + (issued % kDecodeBufs) * TILE, w);
+    const uint32_t dst = lds0 + (issued % kDecodeBufs) * TILE;
     ++issued;
+    if (dq) {
+      dma_tile32<R>(q_lat + ((size_t)db * H + hg * 32) * R, 0, qrows, dst, w);
+      dq = false;
+      return;
+    }
+    const int rb = __builtin_amdgcn_readfirstlane(RB[db]);  // first cache row of sequence db
+    dma_tile32<R>(lat + (size_t)rb * R, dk, dend, dst, w);
     dk += kDecodeTileKeys;
     if (dk >= dend) {
       ++db;
       if (seg_more(db)) {
         dk = 0;
         dend = seg_end(db);
+        dq = true;
       } else {
         ddone = true;
       }
     }
   };
+  // items 0 .. 3: the first query block is read before the loop, so all four
+  // buffers can be in flight at the start
 #pragma unroll
-  for (int t = 0; t < kDecodeBufs - 1; ++t)
+  for (int t = 0; t < kDecodeBufs; ++t)
     if (!ddone) copy_next();
 
   int cb = b_first, ck = k_first, cend = seg_end(b_first);  // compute cursor
   bf16x8 qf[NKS];
-  auto load_q = [&](int b) {
-    const int hh = hg * 32 + 16 * qb + n;
-    const uint16_t* qrow = q_lat + ((size_t)b * H + (hh < H ? hh : H - 1)) * R + 8 * G;
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) qf[ks] = *(const bf16x8*)(qrow + 32 * ks);
-    // Consume the query registers here: the copies are invisible to the
-    // compiler's wait counting, and a query load still pending in the loop
-    // would make it wait on the vector-memory counter every iteration.
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) asm volatile("" : : "v"(qf[ks]));
-  };
-  load_q(cb);
 
   f32x4 o[NCW][2];
   float m_run[2], l_part;
@@ -155,6 +159,16 @@ void decode_split(const uint16_t* __restrict__ q_lat, const uint16_t* __restrict
   const int trsub = 8 * (n & 1);
   const int trh = (n & 3) >> 1;
   char* pw = pbuf + ((qb * 4 + G) * 16 + n) * 16 + kb * 8;  // this lane's 4 probabilities
+  // this lane's query fragments from a landed query block: row 16 qb + n
+  // (tswz(16 + n) = tswz(n)), columns 32 ks + 8 G .. + 7
+  auto read_q = [&](const char* qtile) {
+    const char* qrow = qtile + (16 * qb + n) * (R * 2);
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      const int c = 4 * ks + G;
+      qf[ks] = lds_read16(qrow + 16 * ((c & ~15) | ((c & 15) ^ fs)));
+    }
+  };
 
   // partial state of sequence b's segment into slot g + b: l of every head
   // from the two key halves (through LDS), o normalised, (m, l)
@@ -184,9 +198,12 @@ void decode_split(const uint16_t* __restrict__ q_lat, const uint16_t* __restrict
     }
   };
 
-  dma_wait_tiles<NI>(issued - 1);  // tile 0 landed
+  // items 0 (the first query block) and 1 (the first tile) landed; 2 <= issued
+  // <= 4 since a segment is never empty
+  dma_wait_tiles<NI>(issued - 2);
   __builtin_amdgcn_s_barrier();
-  for (int tau = 0;; ++tau) {
+  read_q(smem);
+  for (int tau = 1;; ++tau) {
     const char* tile = smem + (tau % kDecodeBufs) * TILE;
     const int kt = ck;
 
@@ -213,8 +230,8 @@ void decode_split(const uint16_t* __restrict__ q_lat, const uint16_t* __restrict
       mt = max_xor32(max_xor16(mt));
       if (G == 0) mxbuf[(kb * 2 + qb) * 16 + n] = mt;
     }
-    lds_publish_barrier();  // X: maxima posted; every wave is done with tile tau - 1
-    // refill the buffer of tile tau - 1
+    lds_publish_barrier();  // X: maxima posted; every wave is done with item tau - 1
+    // refill the buffer of item tau - 1
     if (!ddone) copy_next();
     float alpha[2];
     bool grow_any = false;
@@ -262,16 +279,22 @@ void decode_split(const uint16_t* __restrict__ q_lat, const uint16_t* __restrict
       o[c][0] = mfma16x16x32(av, Pq[0], o[c][0]);
       o[c][1] = mfma16x16x32(av, Pq[1], o[c][1]);
     }
-    // ---- advance; at the end of a segment, its partial state and the next query
+    // ---- advance; at the end of a segment, its partial state, then the next
+    // segment's query block (item tau + 1) and first tile (item tau + 2)
     ck += kDecodeTileKeys;
     if (ck >= cend) {
-      flush(cb);
+      flush(cb);  // its barrier: every wave is done with tile tau
       ++cb;
       if (!seg_more(cb)) break;
       ck = 0;
       cend = seg_end(cb);
-      load_q(cb);
       reset();
+      if (!ddone) copy_next();  // refill the buffer of tile tau
+      // items tau + 1 and tau + 2 exist, so issued >= tau + 3
+      dma_wait_tiles<NI>(issued - tau - 3);
+      __builtin_amdgcn_s_barrier();
+      read_q(smem + ((tau + 1) % kDecodeBufs) * TILE);
+      ++tau;
     }
   }
 }
