@@ -107,6 +107,7 @@ void decode_split(const uint16_t* __restrict__ q_lat, const uint16_t* __restrict
   // would drain the stream at every segment start.
   const int qrows = H - hg * 32 < 32 ? H - hg * 32 : 32;  // heads of this group (rows past it repeat the last)
   int db = b_first, dk = k_first, dend = seg_end(b_first);
+  int drb = __builtin_amdgcn_readfirstlane(RB[b_first]);  // first cache row of sequence db
   bool dq = true;  // the next item is the query block of sequence db
   bool ddone = false;
   int issued = 0;
@@ -118,14 +119,14 @@ void decode_split(const uint16_t* __restrict__ q_lat, const uint16_t* __restrict
       dq = false;
       return;
     }
-    const int rb = __builtin_amdgcn_readfirstlane(RB[db]);  // first cache row of sequence db
-    dma_tile32<R>(lat + (size_t)rb * R, dk, dend, dst, w);
+    dma_tile32<R>(lat + (size_t)drb * R, dk, dend, dst, w);
     dk += kDecodeTileKeys;
     if (dk >= dend) {
       ++db;
       if (seg_more(db)) {
         dk = 0;
         dend = seg_end(db);
+        drb = __builtin_amdgcn_readfirstlane(RB[db]);
         dq = true;
       } else {
         ddone = true;
