@@ -41,8 +41,9 @@ __device__ __forceinline__ void dma_wait_tiles(int later) {
 // slot g + b.  Every compute unit thus streams the same number of keys.
 //
 // A segment [k0, k1) of sequence b is streamed through a ring of
-// kDecodeBufs block-shared LDS tiles of 32 keys (three in flight while one is
-// read).  The four waves share each tile: wave
+// kDecodeBufs block-shared LDS buffers (three in flight while one is read):
+// first the query block of sequence b, then its tiles of 32 keys.  The four
+// waves share each tile: wave
 // w = 2 kb + qb computes the 16 x 16 score block of keys
 // 16 kb .. 16 kb + 15 and heads 16 qb .. 16 qb + 15; the row maxima and the
 // probabilities P are exchanged through LDS; then wave w accumulates o_lat
