@@ -10,7 +10,10 @@ H=32) is timed in the same run and reported in the `decode` object.
 Prints ONE JSON line.  `value` is prefill TFLOP/s of the absorbed method's
 algorithmic work (causal keys only); `roofline` is the flash kernel's
 achieved TFLOP/s against the dense bf16 matrix-core peak, from its
-average launch time measured with HIP events on the launch stream;
+average launch time measured with HIP events on the launch stream, with
+`traffic` (HBM bytes per launch) and `mfma_busy` (the matrix cores' busy
+fraction) read from the committed rocprofv3 counter summaries under
+profiles/ while they match the library sources;
 `cpu_baseline` is the fp64 CPU oracle timed on a bounded sample of the same
 workload.
 """
@@ -31,6 +34,7 @@ PEAK_BF16_TFLOPS = 2516.6     # 256 CU x 2.4 GHz x 4096 dense bf16 FLOP/clk/CU
 PEAK_HBM_GBS = 8000.0         # HBM3E
 PEAK_FP32_TFLOPS = 157.3      # 256 CU x 2.4 GHz x 256 fp32 FLOP/clk/CU (vector ALUs)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+MFMA_FILE = os.path.join(ROOT, "profiles", "mfma_util.json")
 
 
 def library_source_sha() -> str:
@@ -55,6 +59,21 @@ def measured_traffic(kernel: str):
         return None
     k = t.get("kernels", {}).get(kernel)
     return None if k is None else int(k["hbm_bytes"])
+
+
+def measured_mfma_busy(kernel: str):
+    """Fraction of the run's SIMD cycles the matrix cores were busy in
+    `kernel` (rocprofv3 MfmaUtil, committed summary), or None when the
+    library sources changed since it was taken."""
+    try:
+        with open(MFMA_FILE) as fh:
+            t = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_sha256_16") != library_source_sha():
+        return None
+    k = t.get("kernels", {}).get(kernel)
+    return None if k is None else float(k["mfma_busy"])
 
 
 # ---------------------------------------------------------------- algorithmic work
@@ -310,6 +329,7 @@ def main(argv=None):
         ach = work["attn"] / (flash["avg_ms"] * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": measured_traffic("flash_latent_bf16"),
+                "mfma_busy": measured_mfma_busy("flash_latent_bf16"),
                 "kernel": "flash_latent_bf16", "avg_ms": round(flash["avg_ms"], 4),
                 "flops_per_launch": work["attn"]}
     line = {
@@ -349,7 +369,7 @@ def main(argv=None):
             ach = uw["attn"] / (mha["avg_ms"] * 1e-3) / 1e12
             uroof = {"bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": measured_traffic("flash_mha_bf16"),
-                     "kernel": "flash_mha_bf16", "avg_ms": round(mha["avg_ms"], 4), "flops_per_launch": uw["attn"]}
+                     "mfma_busy": measured_mfma_busy("flash_mha_bf16"), "kernel": "flash_mha_bf16", "avg_ms": round(mha["avg_ms"], 4), "flops_per_launch": uw["attn"]}
         line["unabsorbed"] = {
             "what": "the same prefill with k and v materialised (mla_latent_attn_fwd_unabsorbed); value counts "
                     "that form's own FLOPs",
@@ -370,7 +390,8 @@ def main(argv=None):
                 "bound": "mfma", "achieved": round(mw["attn"] / (mflash["avg_ms"] * 1e-3) / 1e12, 2),
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(mw["attn"] / (mflash["avg_ms"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
-                "traffic": measured_traffic("flash_latent_bf16_masked"), "kernel": "flash_latent_bf16_masked",
+                "traffic": measured_traffic("flash_latent_bf16_masked"),
+                "mfma_busy": measured_mfma_busy("flash_latent_bf16_masked"), "kernel": "flash_latent_bf16_masked",
                 "avg_ms": round(mflash["avg_ms"], 4), "flops_per_launch": mw["attn"]},
             "kernels_ms": {k: round(v["avg_ms"], 4) for k, v in mkt.items()}}
     if not args.no_full:
