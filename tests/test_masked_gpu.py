@@ -156,3 +156,30 @@ def test_bf16_long_prefill_masked_sampled():
     rel = float(np.sqrt(np.nanmean((got - ref) ** 2) / np.nanmean(ref ** 2)))
     print(f"{len(rb)} sampled rows, max abs err {err:.3e}, rel rms {rel:.3e}")
     assert rel < 4e-3
+
+
+def test_masked_beyond_int32_offsets_sampled():
+    """B=4, T=16400, H=64, r=512 with a padding-plus-holes mask: q_lat and
+    o_lat hold more than 2^31 elements, so the rows of batch 3 from
+    t = 16336 on sit past every 32-bit element offset.  Sampled rows either
+    side of that line, in the last batch and another, against the oracle."""
+    import torch
+    cfg = cfg_like("bf16_long_prefill", B=4, T=16400)
+    assert cfg.B * cfg.T * cfg.H * cfg.r > 2 ** 31
+    inp = synth.make_inputs(cfg)
+    mask = synth.make_key_mask(cfg, p_hole=0.05)
+    mask[3, :] = 1
+    mask[3, 100:140] = 0                      # batch 3: every row past 140 sees all but 40 keys
+    print(f"masked prefill past 32-bit offsets {cfg}", flush=True)
+    out, _ = run_masked(cfg, inp, mask)
+    first_past = 2 ** 31 // (cfg.H * cfg.r) - 3 * cfg.T
+    rb, rh, rt = [], [], []
+    for (b, h) in [(3, 0), (3, 63), (1, 9)]:
+        for t in sorted({0, 99, 100, 139, 140, first_past - 1, first_past, first_past + 1, cfg.T - 1}):
+            rb.append(b); rh.append(h); rt.append(t)
+    rb, rh, rt = map(np.array, (rb, rh, rt))
+    ref = oracle.attend_rows(inp["q"][rb, rt, rh], rb, rh, rt + 1, inp["kv_latent"], inp["w_up_k"], inp["w_up_v"],
+                             cfg.scale, key_mask=mask)
+    got = to_f64(out[torch.from_numpy(rb).cuda(), torch.from_numpy(rt).cuda(), torch.from_numpy(rh).cuda()])
+    err = compare_nan(got, ref, cfg.dtype, cfg.name)
+    print(f"{len(rb)} sampled rows, max abs err {err:.3e}")
