@@ -13,7 +13,8 @@ P = 1 << 20   # a 16-byte aligned fake address: never dereferenced on these path
 
 
 def declared_symbols():
-    text = open(os.path.join(ROOT, "include", "mla.h")).read()
+    with open(os.path.join(ROOT, "include", "mla.h")) as fh:
+        text = fh.read()
     return sorted(set(re.findall(r"^\s*(?:mla_status|size_t|int|const char\*)\s+(mla_\w+)\s*\(", text, re.M)))
 
 

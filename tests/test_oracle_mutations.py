@@ -39,7 +39,8 @@ MUTANTS = {
 @pytest.mark.parametrize("name", sorted(MUTANTS))
 def test_mutant_is_caught(name, tmp_path):
     old, new = MUTANTS[name]
-    src = open(SRC).read()
+    with open(SRC) as fh:
+        src = fh.read()
     assert src.count(old) >= 1, f"mutation site for {name} not found"
     mutated = tmp_path / "mutant.cpp"
     mutated.write_text(src.replace(old, new))
