@@ -49,7 +49,10 @@ def _problem(seed, B, T, H, d, r):
 def _close(a, b, rtol, atol, what):
     a, b = np.asarray(a), np.asarray(b)
     bad = ~(np.abs(a - b) <= atol + rtol * np.abs(b))
-    assert not bad.any(), f"{what}: {bad.sum()} mismatches, max abs err {np.nanmax(np.abs(a - b))}"
+    if bad.any():
+        err = np.abs(a - b)
+        worst = np.max(err[np.isfinite(err)]) if np.isfinite(err).any() else float("nan")
+        raise AssertionError(f"{what}: {bad.sum()} mismatches, max finite abs err {worst}")
 
 
 def pin_brute_force_scalar(lib):
