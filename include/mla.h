@@ -179,7 +179,8 @@ size_t mla_decode_varlen_workspace_size(int B, int total, int H, int d, int r, m
  * cu_seqlens[b] .. cu_seqlens[b+1]-1 of kv_latent [total, r] instead of a
  * padded [B, Tmax, r].
  *   cu_seqlens [B+1] int32 in DEVICE memory, 0 <= cu_seqlens[b] < cu_seqlens[b+1] <= total
- *   (every sequence non-empty).  The host does not inspect it; out of that
+ *   (every sequence non-empty); B * total must stay below 2^31
+ *   (MLA_ERR_UNSUPPORTED otherwise), as B * Tmax for the padded layout.  The host does not inspect it; out of that
  *   contract each sequence is clamped into the cache (first row into [0, total),
  *   length into [1, total - first row]), so no read leaves kv_latent, but the
  *   result is unspecified.
@@ -202,6 +203,27 @@ mla_status mla_decode_varlen_fwd(const void* q, const void* kv_latent, const int
  * of the attended keys of the following decode. */
 mla_status mla_kv_append(void* kv_cache, int32_t* seq_lens, const void* new_latent, int B, int Tmax,
                          int r, mla_dtype dt, void* stream);
+
+/* The number of chunks the decode split cuts the concatenated caches of one
+ * call into, per group of 32 heads, for later mla_decode_fwd and
+ * mla_decode_varlen_fwd calls of this process: 0 (the default) takes one
+ * chunk per compute unit; 1 .. 1024 fixes the count.  The result is the same
+ * up to rounding for every count (the partial softmax states are merged by
+ * log-sum-exp, an associative combination: POPCORNBENCH page Kimi-K2.6
+ * l2_p29, its online-softmax derivation); it exists for tuning and for
+ * testing that invariance.  Returns MLA_ERR_INVALID_ARGUMENT outside
+ * [0, 1024].  Process-wide; safe to call from any thread, but calls that
+ * overlap a decode on another thread may see either count. */
+mla_status mla_decode_set_splits(int splits);
+
+/* Replace the device's per-block LDS limit that the argument checks compare
+ * each kernel's LDS need against (0, the default, queries the device).  A
+ * limit below a kernel's need makes the call fail with MLA_ERR_UNSUPPORTED
+ * before anything is enqueued -- the check that keeps a launch from failing
+ * on shared memory, as the KV-compression page's kernel did (POPCORNBENCH
+ * page FW-GLM-5-1 l2_p1, its launch-failure passage).  For testing that
+ * error path, including on a host without a device; process-wide. */
+mla_status mla_set_lds_limit_override(size_t bytes);
 
 /* Per-kernel timing, for benchmarking (not part of the computation).
  * mla_profile_enable(1) makes every later kernel launch of the library record

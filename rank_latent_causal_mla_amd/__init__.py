@@ -24,8 +24,8 @@ EXPORTED = ("mla_down_proj", "mla_latent_attn_workspace_size", "mla_latent_attn_
             "mla_latent_attn_auto_form", "mla_latent_attn_auto_workspace_size", "mla_latent_attn_fwd_auto",
             "mla_latent_attn_unabsorbed_workspace_size", "mla_latent_attn_fwd_unabsorbed",
             "mla_decode_workspace_size", "mla_decode_fwd", "mla_decode_varlen_workspace_size",
-            "mla_decode_varlen_fwd", "mla_kv_append", "mla_profile_enable", "mla_profile_collect",
-            "mla_status_string", "mla_last_error")
+            "mla_decode_varlen_fwd", "mla_kv_append", "mla_decode_set_splits", "mla_set_lds_limit_override",
+            "mla_profile_enable", "mla_profile_collect", "mla_status_string", "mla_last_error")
 
 _lib = None
 
@@ -90,6 +90,10 @@ def load():
     lib.mla_decode_varlen_fwd.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, i32, vp, sz, vp]
     lib.mla_kv_append.restype = i32
     lib.mla_kv_append.argtypes = [vp, vp, vp, i32, i32, i32, i32, vp]
+    lib.mla_decode_set_splits.restype = i32
+    lib.mla_decode_set_splits.argtypes = [i32]
+    lib.mla_set_lds_limit_override.restype = i32
+    lib.mla_set_lds_limit_override.argtypes = [sz]
     lib.mla_status_string.restype = ctypes.c_char_p
     lib.mla_status_string.argtypes = [i32]
     lib.mla_last_error.restype = ctypes.c_char_p
@@ -199,6 +203,16 @@ def mla_kv_append_raw(kv_cache, seq_lens, new_latent, B, Tmax, r, dt, stream=0):
     return load().mla_kv_append(kv_cache, seq_lens, new_latent, B, Tmax, r, dt, stream)
 
 
+def mla_decode_set_splits(splits: int = 0):
+    """Chunks per 32-head group of the decode split for later decode calls (0 = one per compute unit)."""
+    _check(load().mla_decode_set_splits(int(splits)))
+
+
+def mla_set_lds_limit_override(nbytes: int = 0):
+    """Per-block LDS limit the argument checks use instead of the device's (0 = query the device)."""
+    _check(load().mla_set_lds_limit_override(int(nbytes)))
+
+
 def mla_profile_enable(on: bool = True):
     _check(load().mla_profile_enable(1 if on else 0))
 
@@ -245,12 +259,67 @@ def _shaped(t, shape, dtype, name):
         raise ValueError(f"{name} must be {list(shape)} {dtype}, got {list(t.shape)} {t.dtype}")
 
 
+# The C ABI takes plain pointers and sizes and cannot see the tensors' shapes,
+# so the wrappers check here, before anything is enqueued, that every input
+# has the shape and dtype the sizes it passes imply: a mismatch would make the
+# kernels read or write outside a tensor.
+
+def _want(t, shape, name):
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must be {list(shape)}, got {list(t.shape)}")
+
+
+def _same_float(*named):
+    """All tensors share one float dtype (float32 or bfloat16)."""
+    (n0, t0), rest = named[0], named[1:]
+    _dt(t0)
+    for n, t in rest:
+        if t.dtype != t0.dtype:
+            raise ValueError(f"{n} must be {t0.dtype} like {n0}, got {t.dtype}")
+
+
+def _int32_vec(t, n, name):
+    import torch
+    if t.dtype != torch.int32 or t.dim() != 1 or t.numel() != n:
+        raise ValueError(f"{name} must be int32 [{n}], got {t.dtype} {list(t.shape)}")
+
+
+def _prefill_dims(q, kv_latent, w_up_k, w_up_v):
+    """q [B,T,H,d], kv_latent [B,T,r], w_up_k / w_up_v [r,H,d] -> (B, T, H, d, r)."""
+    if q.dim() != 4:
+        raise ValueError(f"q must be [B, T, H, d], got {list(q.shape)}")
+    B, T, H, d = q.shape
+    if kv_latent.dim() != 3:
+        raise ValueError(f"kv_latent must be [B, T, r], got {list(kv_latent.shape)}")
+    r = kv_latent.shape[-1]
+    _want(kv_latent, (B, T, r), "kv_latent")
+    _want(w_up_k, (r, H, d), "w_up_k")
+    _want(w_up_v, (r, H, d), "w_up_v")
+    _same_float(("q", q), ("kv_latent", kv_latent), ("w_up_k", w_up_k), ("w_up_v", w_up_v))
+    return B, T, H, d, r
+
+
+def _decode_dims(q, w_up_k, w_up_v, r):
+    """q [B,1,H,d], w_up_k / w_up_v [r,H,d] -> (B, H, d)."""
+    if q.dim() != 4 or q.shape[1] != 1:
+        raise ValueError(f"q must be [B, 1, H, d], got {list(q.shape)}")
+    B, _, H, d = q.shape
+    _want(w_up_k, (r, H, d), "w_up_k")
+    _want(w_up_v, (r, H, d), "w_up_v")
+    return B, H, d
+
+
 def mla_down_proj(hidden, w_down, kv_latent=None, stream=None):
     """kv_latent[B,T,r] = hidden[B,T,D] @ w_down[D,r]."""
     import torch
-    _dev(hidden, w_down)
+    if hidden.dim() != 3 or w_down.dim() != 2:
+        raise ValueError(f"hidden must be [B, T, D] and w_down [D, r], got {list(hidden.shape)}, "
+                         f"{list(w_down.shape)}")
     B, T, D = hidden.shape
     r = w_down.shape[1]
+    _want(w_down, (D, r), "w_down")
+    _same_float(("hidden", hidden), ("w_down", w_down))
+    _dev(hidden, w_down)
     if kv_latent is None:
         kv_latent = torch.empty((B, T, r), dtype=hidden.dtype, device=hidden.device)
     _shaped(kv_latent, (B, T, r), hidden.dtype, "kv_latent")
@@ -263,9 +332,8 @@ def mla_down_proj(hidden, w_down, kv_latent=None, stream=None):
 def mla_latent_attn_fwd(q, kv_latent, w_up_k, w_up_v, out=None, scale=None, workspace=None, stream=None):
     """Causal latent attention, prefill: q[B,T,H,d], kv_latent[B,T,r], w_up_k/w_up_v[r,H,d] -> out[B,T,H,d]."""
     import torch
+    B, T, H, d, r = _prefill_dims(q, kv_latent, w_up_k, w_up_v)
     _dev(q, kv_latent, w_up_k, w_up_v)
-    B, T, H, d = q.shape
-    r = kv_latent.shape[-1]
     dt = _dt(q)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
@@ -287,15 +355,14 @@ def mla_latent_attn_fwd_masked(q, kv_latent, key_mask, w_up_k, w_up_v, out=None,
     """Causal prefill with a key mask: key_mask[B,T] (uint8 or bool, device; nonzero = visible).
     A query row with no visible key s <= t comes out NaN."""
     import torch
-    _dev(q, kv_latent, key_mask, w_up_k, w_up_v)
-    B, T, H, d = q.shape
-    r = kv_latent.shape[-1]
+    B, T, H, d, r = _prefill_dims(q, kv_latent, w_up_k, w_up_v)
     if tuple(key_mask.shape) != (B, T):
-        raise ValueError("key_mask must be [B, T]")
+        raise ValueError(f"key_mask must be [B, T] = [{B}, {T}], got {list(key_mask.shape)}")
     if key_mask.dtype == torch.bool:
         key_mask = key_mask.view(torch.uint8)
     if key_mask.dtype != torch.uint8:
         raise TypeError("key_mask must be uint8 or bool")
+    _dev(q, kv_latent, key_mask, w_up_k, w_up_v)
     dt = _dt(q)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
@@ -316,9 +383,8 @@ def mla_latent_attn_fwd_masked(q, kv_latent, key_mask, w_up_k, w_up_v, out=None,
 def mla_latent_attn_fwd_auto(q, kv_latent, w_up_k, w_up_v, out=None, scale=None, workspace=None, stream=None):
     """The causal prefill in the form the library picks for the shape (mla_latent_attn_auto_form)."""
     import torch
+    B, T, H, d, r = _prefill_dims(q, kv_latent, w_up_k, w_up_v)
     _dev(q, kv_latent, w_up_k, w_up_v)
-    B, T, H, d = q.shape
-    r = kv_latent.shape[-1]
     dt = _dt(q)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
@@ -339,9 +405,8 @@ def mla_latent_attn_fwd_unabsorbed(q, kv_latent, w_up_k, w_up_v, out=None, scale
                                    stream=None):
     """The same prefill in unabsorbed form (k, v materialised; bf16, d = 128, r in {128, 256, 512})."""
     import torch
+    B, T, H, d, r = _prefill_dims(q, kv_latent, w_up_k, w_up_v)
     _dev(q, kv_latent, w_up_k, w_up_v)
-    B, T, H, d = q.shape
-    r = kv_latent.shape[-1]
     dt = _dt(q)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
@@ -362,11 +427,15 @@ def mla_latent_attn_fwd_unabsorbed(q, kv_latent, w_up_k, w_up_v, out=None, scale
 def mla_decode_fwd(q, kv_latent, seq_lens, w_up_k, w_up_v, out=None, scale=None, workspace=None, stream=None):
     """Decode: q[B,1,H,d], kv_latent[B,Tmax,r], seq_lens[B] int32 (device) -> out[B,1,H,d]."""
     import torch
-    _dev(q, kv_latent, seq_lens, w_up_k, w_up_v)
-    if seq_lens.dtype != torch.int32:
-        raise TypeError("seq_lens must be int32")
+    if kv_latent.dim() != 3:
+        raise ValueError(f"kv_latent must be [B, Tmax, r], got {list(kv_latent.shape)}")
     B, Tmax, r = kv_latent.shape
-    H, d = w_up_k.shape[1], w_up_k.shape[2]
+    Bq, H, d = _decode_dims(q, w_up_k, w_up_v, r)
+    if Bq != B:
+        raise ValueError(f"q must be [B={B}, 1, H, d] like kv_latent, got {list(q.shape)}")
+    _int32_vec(seq_lens, B, "seq_lens")
+    _same_float(("q", q), ("kv_latent", kv_latent), ("w_up_k", w_up_k), ("w_up_v", w_up_v))
+    _dev(q, kv_latent, seq_lens, w_up_k, w_up_v)
     dt = _dt(q)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
@@ -388,13 +457,13 @@ def mla_decode_varlen_fwd(q, kv_latent, cu_seqlens, w_up_k, w_up_v, out=None, sc
                           stream=None):
     """Decode over a packed cache: q[B,1,H,d], kv_latent[total,r], cu_seqlens[B+1] int32 (device) -> out[B,1,H,d]."""
     import torch
-    _dev(q, kv_latent, cu_seqlens, w_up_k, w_up_v)
-    if cu_seqlens.dtype != torch.int32 or not cu_seqlens.is_contiguous():
-        raise ValueError("cu_seqlens must be contiguous int32")
-    B, _, H, d = q.shape
+    if kv_latent.dim() != 2:
+        raise ValueError(f"kv_latent must be [total, r], got {list(kv_latent.shape)}")
     total, r = kv_latent.shape
-    if cu_seqlens.numel() != B + 1:
-        raise ValueError("cu_seqlens needs B + 1 entries")
+    B, H, d = _decode_dims(q, w_up_k, w_up_v, r)
+    _int32_vec(cu_seqlens, B + 1, "cu_seqlens")
+    _same_float(("q", q), ("kv_latent", kv_latent), ("w_up_k", w_up_k), ("w_up_v", w_up_v))
+    _dev(q, kv_latent, cu_seqlens, w_up_k, w_up_v)
     dt = _dt(q)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
@@ -414,13 +483,13 @@ def mla_decode_varlen_fwd(q, kv_latent, cu_seqlens, w_up_k, w_up_v, out=None, sc
 
 def mla_kv_append(kv_cache, seq_lens, new_latent, stream=None):
     """kv_cache[B,Tmax,r] and seq_lens[B] int32 (device) updated in place with new_latent[B,r]."""
-    import torch
-    _dev(kv_cache, seq_lens, new_latent)
-    if seq_lens.dtype != torch.int32 or not seq_lens.is_contiguous():
-        raise ValueError("seq_lens must be contiguous int32")
+    if kv_cache.dim() != 3:
+        raise ValueError(f"kv_cache must be [B, Tmax, r], got {list(kv_cache.shape)}")
     B, Tmax, r = kv_cache.shape
-    if tuple(new_latent.shape) != (B, r) or new_latent.dtype != kv_cache.dtype:
-        raise ValueError("new_latent must be [B, r] in the cache's dtype")
+    _int32_vec(seq_lens, B, "seq_lens")
+    _want(new_latent, (B, r), "new_latent")
+    _same_float(("kv_cache", kv_cache), ("new_latent", new_latent))
+    _dev(kv_cache, seq_lens, new_latent)
     _check(mla_kv_append_raw(kv_cache.data_ptr(), seq_lens.data_ptr(), new_latent.data_ptr(), B, Tmax, r,
                              _dt(kv_cache), _stream(stream)))
     return kv_cache
@@ -431,11 +500,15 @@ def mla_latent_attn_fwd_full(hidden, w_down, q, w_up_k, w_up_v, kv_latent=None, 
     """Full path in one call: kv_latent[B,T,r] = hidden[B,T,D] @ w_down[D,r] (written: the latent
     cache), then causal latent attention -> out[B,T,H,d].  Returns (out, kv_latent)."""
     import torch
-    _dev(hidden, w_down, q, w_up_k, w_up_v)
+    if q.dim() != 4 or w_down.dim() != 2:
+        raise ValueError(f"q must be [B, T, H, d] and w_down [D, r], got {list(q.shape)}, {list(w_down.shape)}")
     B, T, H, d = q.shape
     D, r = w_down.shape
-    if tuple(hidden.shape) != (B, T, D):
-        raise ValueError("hidden must be [B, T, D]")
+    _want(hidden, (B, T, D), "hidden")
+    _want(w_up_k, (r, H, d), "w_up_k")
+    _want(w_up_v, (r, H, d), "w_up_v")
+    _same_float(("q", q), ("hidden", hidden), ("w_down", w_down), ("w_up_k", w_up_k), ("w_up_v", w_up_v))
+    _dev(hidden, w_down, q, w_up_k, w_up_v)
     dt = _dt(q)
     if scale is None:
         scale = 1.0 / math.sqrt(d)

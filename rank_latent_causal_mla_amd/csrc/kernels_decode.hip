@@ -12,6 +12,7 @@
 //                       (b, h), then the W_uv up-projection on the matrix unit.
 #include "mla_device.h"
 #include "mla_kernels.h"
+#include "host_once.h"
 #include "lds_tiles.h"
 #include "prep_blocks.h"
 #include "profile.h"
@@ -451,16 +452,27 @@ __global__ __launch_bounds__(1024) void decode_merge_up(const uint16_t* __restri
 }
 
 // ---------------------------------------------------------------------------
-static int device_cus() {
-  static int cus = 0;
-  if (cus == 0) {
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
-      cus = 256;
+int device_cus() {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<int> cache[kMaxDevices];  // 0 = not queried yet
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  std::atomic<int>* slot = dev >= 0 && dev < kMaxDevices ? &cache[dev] : nullptr;
+  if (slot) {
+    const int c = slot->load(std::memory_order_relaxed);
+    if (c > 0) return c;
   }
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) cus = 256;
+  if (slot) slot->store(cus, std::memory_order_relaxed);  // racing callers store the same value
   return cus;
 }
+
+namespace {
+std::atomic<int> g_decode_splits{0};
+}  // namespace
+int decode_splits_override() { return g_decode_splits.load(std::memory_order_relaxed); }
+void set_decode_splits(int p) { g_decode_splits.store(p, std::memory_order_relaxed); }
 
 size_t decode_max_splits(int B) { return (size_t)decode_split_cap() + B; }
 
@@ -469,18 +481,18 @@ static hipError_t run_decode(const uint16_t* q, const uint16_t* lat, const int32
                              const uint16_t* wk, const uint16_t* wv, uint16_t* out, int B, int Tmax,
                              int H, int d, float sl2, uint16_t* q_lat, uint16_t* part_o, float* part_ml,
                              uint16_t* wvT, int32_t* S, int32_t* RB, hipStream_t st) {
-  // one chunk of keys per compute unit over all head groups
+  // one chunk of keys per compute unit over all head groups (or the count set
+  // by mla_decode_set_splits)
   const int nhg = (H + 31) / 32;
-  int P = device_cus() / nhg;
+  const int forced = decode_splits_override();
+  int P = forced > 0 ? forced : device_cus() / nhg;
   P = P < 1 ? 1 : (P > decode_split_cap() ? decode_split_cap() : P);
   const size_t lds = decode_lds_bytes(R);
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)decode_split<R>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       (int)lds);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  static OnceFlag attrs;
+  const hipError_t e = run_once(attrs, [lds] {
+    return hipFuncSetAttribute((const void*)decode_split<R>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  });
+  if (e != hipSuccess) return e;
   {
     ProfScope ps("decode_prep", st);
     const int nabs = ((B + 31) / 32) * H * (R / 128);

@@ -16,6 +16,7 @@
 #include "lds_tiles.h"
 #include "prep_blocks.h"
 #include "profile.h"
+#include "host_once.h"
 
 namespace mla {
 
@@ -444,8 +445,8 @@ struct Flash {
 // order (zero rows after them) and cnt [B][T] the number of visible keys
 // s <= t: query t then attends packed keys 0 .. cnt[b][t] - 1, which are its
 // visible keys, through the same causal limit.  A row with no visible key
-// (cnt = 0) masks every key, ends with l = 0 and stores 0 / 0 = NaN, the
-// value the softmax of an all -infinity row takes.
+// (cnt = 0) masks every key and ends with l = 0; its output is written as
+// NaN, the value the softmax of an all -infinity row takes.
 template <int R, bool COMPACT>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
 void flash_latent_bf16(const uint16_t* __restrict__ q_lat, const uint16_t* __restrict__ lat,
@@ -552,7 +553,9 @@ void flash_latent_bf16(const uint16_t* __restrict__ q_lat, const uint16_t* __res
       *(__attribute__((address_space(3))) bf16x8*)(uintptr_t)(pbuf + ((2 * w + qb) * 64 + lane) * 16) = P[qb];
       if (G == 0) abuf[(2 * w + qb) * 16 + n] = alpha[qb];
     }
-    if (lane == 0) fbuf[w] = __builtin_amdgcn_ballot_w64(grow) != 0;
+    // every lane votes: a ballot inside the lane-0 branch would see lane 0's row only
+    const uint64_t grew = __builtin_amdgcn_ballot_w64(grow);
+    if (lane == 0) fbuf[w] = grew != 0;
     lds_publish_barrier();  // P and rescale factors of tile j posted
     {
       const u32x4 f = *(const __attribute__((address_space(3))) u32x4*)(uintptr_t)fbuf;
@@ -625,13 +628,16 @@ void flash_latent_bf16(const uint16_t* __restrict__ q_lat, const uint16_t* __res
   static_assert(128 * OS <= kFlashBufs * TILE + F::NQ * 1024, "the staged rows fit the ring and the P buffer");
 #pragma unroll
   for (int q = 0; q < F::NQ; ++q) {
-    const float inv = 1.f / abuf[q * 16 + en];
+    const float l = abuf[q * 16 + en];
+    const float inv = 1.f / l;
     char* srow = smem + (16 * q + en) * OS + 2 * (cw + 4 * eG);
 #pragma unroll
     for (int c = 0; c < F::NCW; ++c) {
       mfma_agpr_tie(o[c][q]);
-      *(__attribute__((address_space(3))) u32x2*)(uintptr_t)(srow + 32 * c) =
-          u32x2{pack_bf16x2(o[c][q][0] * inv, o[c][q][1] * inv), pack_bf16x2(o[c][q][2] * inv, o[c][q][3] * inv)};
+      // a row with no visible key (l = 0) is NaN, written as such (bf16 quiet NaN bits)
+      const uint32_t lo = l > 0.f ? pack_bf16x2(o[c][q][0] * inv, o[c][q][1] * inv) : 0x7fc07fc0u;
+      const uint32_t hi = l > 0.f ? pack_bf16x2(o[c][q][2] * inv, o[c][q][3] * inv) : 0x7fc07fc0u;
+      *(__attribute__((address_space(3))) u32x2*)(uintptr_t)(srow + 32 * c) = u32x2{lo, hi};
     }
   }
   lds_publish_barrier();
@@ -808,20 +814,20 @@ static hipError_t run_prefill(const uint16_t* q, const uint16_t* lat, const uint
                               const uint8_t* key_mask, int32_t* cnt, int32_t* src, uint16_t* lat_c,
                               hipStream_t st) {
   const int N = B * T;
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)flash_latent_bf16<R, false>,
+  static OnceFlag attrs;
+  hipError_t e = run_once(attrs, [] {
+    hipError_t r = hipFuncSetAttribute((const void*)flash_latent_bf16<R, false>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)flash_lds_bytes(R));
-    if (e == hipSuccess)
-      e = hipFuncSetAttribute((const void*)flash_latent_bf16<R, true>,
+    if (r == hipSuccess)
+      r = hipFuncSetAttribute((const void*)flash_latent_bf16<R, true>,
                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)flash_lds_bytes(R));
-    if (e == hipSuccess)
-      e = hipFuncSetAttribute((const void*)up_bf16<R, false>, hipFuncAttributeMaxDynamicSharedMemorySize,
+    if (r == hipSuccess)
+      r = hipFuncSetAttribute((const void*)up_bf16<R, false>, hipFuncAttributeMaxDynamicSharedMemorySize,
                               (int)up_lds_bytes<R>());
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
-  hipError_t e = absorb_mfma(q, wk, q_lat, N, H, d, R, sl2, st);
+    return r;
+  });
+  if (e != hipSuccess) return e;
+  e = absorb_mfma(q, wk, q_lat, N, H, d, R, sl2, st);
   if (e != hipSuccess) return e;
   {
     ProfScope ps("transpose_wv", st);
@@ -883,14 +889,12 @@ template <int R>
 static hipError_t run_materialise(const uint16_t* lat, const uint16_t* wk, const uint16_t* wv, uint16_t* k,
                                   uint16_t* v, uint16_t* wkT, uint16_t* wvT, int N, int H, int d, float kscale,
                                   hipStream_t st) {
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)up_bf16<R, true>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       (int)up_lds_bytes<R>());
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
-  hipError_t e;
+  static OnceFlag attrs;
+  hipError_t e = run_once(attrs, [] {
+    return hipFuncSetAttribute((const void*)up_bf16<R, true>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                               (int)up_lds_bytes<R>());
+  });
+  if (e != hipSuccess) return e;
   {
     ProfScope ps("transpose_wv", st);
     e = transpose_wv_launch(wk, wkT, R, H, d, st);

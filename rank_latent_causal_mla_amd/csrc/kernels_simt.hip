@@ -6,6 +6,7 @@
 // hidden @ w_down).
 #include "mla_device.h"
 #include "mla_kernels.h"
+#include "host_once.h"
 #include "profile.h"
 
 namespace mla {
@@ -101,7 +102,9 @@ __global__ void attend_simt(const float* __restrict__ q_lat, const T* __restrict
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     const int rho = lane + 64 * i;
-    if (rho < R) o_lat[row * R + rho] = o[i] * inv;
+    // a row with no visible key (l = 0, key mask) is NaN, written as such
+    // (chosen in the integer domain, so no float rule can drop it)
+    if (rho < R) o_lat[row * R + rho] = __uint_as_float(l > 0.f ? __float_as_uint(o[i] * inv) : 0x7fc00000u);
   }
 }
 
@@ -258,13 +261,12 @@ __global__ __launch_bounds__(256) void attend_f32_tiled(const float* __restrict_
 template <int R, typename T>
 static hipError_t attend_f32_tiled_launch(const float* q_lat, const T* lat, float* o_lat, int B, int Tn, int H,
                                           float sl2, hipStream_t st) {
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)attend_f32_tiled<R, T>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)attend_f32_lds_bytes<R>());
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  static OnceFlag attrs;
+  const hipError_t e = run_once(attrs, [] {
+    return hipFuncSetAttribute((const void*)attend_f32_tiled<R, T>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                               (int)attend_f32_lds_bytes<R>());
+  });
+  if (e != hipSuccess) return e;
   const long TH = (long)Tn * H;
   hipLaunchKernelGGL((attend_f32_tiled<R, T>), dim3((unsigned)((TH + kF32Rows - 1) / kF32Rows), B), dim3(256),
                      attend_f32_lds_bytes<R>(), st, q_lat, lat, o_lat, Tn, H, sl2);

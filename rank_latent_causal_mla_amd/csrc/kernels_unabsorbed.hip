@@ -7,6 +7,7 @@
 #include "lds_tiles.h"
 #include "mla_device.h"
 #include "mla_kernels.h"
+#include "host_once.h"
 #include "profile.h"
 
 namespace mla {
@@ -372,13 +373,12 @@ hipError_t prefill_unabsorbed(const void* q, const void* lat, const void* wk, co
   hipError_t e = materialise_kv((const uint16_t*)lat, (const uint16_t*)wk, (const uint16_t*)wv, kk, vv, wkT, wvT,
                                 B * T, H, d, r, sl2, st);
   if (e != hipSuccess) return e;
-  static bool attr_set = false;
-  if (!attr_set) {
-    e = hipFuncSetAttribute((const void*)flash_mha_bf16<128>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                            (int)mha_lds_bytes<128>());
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  static OnceFlag attrs;
+  e = run_once(attrs, [] {
+    return hipFuncSetAttribute((const void*)flash_mha_bf16<128>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                               (int)mha_lds_bytes<128>());
+  });
+  if (e != hipSuccess) return e;
   const int nqb = (T + kMhaRows - 1) / kMhaRows;
   {
     ProfScope ps("flash_mha_bf16", st);

@@ -1,5 +1,6 @@
 // C ABI of the library: argument checks, workspace sizing, path selection
 // and launch sequencing.  Declarations and the contract are in include/mla.h.
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -49,7 +50,14 @@ mla_status check_dims(int B, int T, int H, int d, int r, mla_dtype dt, const cha
 
 bool use_mfma(mla_dtype dt, int d, int r) { return dt == MLA_DTYPE_BF16 && mla::mfma_supported(d, r); }
 
+std::atomic<size_t> g_lds_limit_override{0};  // mla_set_lds_limit_override(); 0 = query the device
+
 mla_status device_lds_limit(size_t* bytes) {
+  const size_t forced = g_lds_limit_override.load(std::memory_order_relaxed);
+  if (forced > 0) {
+    *bytes = forced;
+    return MLA_OK;
+  }
   int dev = 0, v = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e == hipSuccess) e = hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerBlock, dev);
@@ -291,9 +299,11 @@ mla_status decode_common(const void* q, const void* kv_latent, const int32_t* se
   if (!q || !kv_latent || !(seq_lens || cu) || !w_up_k || !w_up_v || !out || !workspace)
     return fail(MLA_ERR_INVALID_ARGUMENT, "null pointer");
   const int32_t* ints = cu ? cu : seq_lens;
-  mla_status s = cu ? check_dims(B, 1, H, d, r, dt, "T") : check_dims(B, rows, H, d, r, dt, "Tmax");
-  if (s != MLA_OK) return s;
   if (cu && rows < 1) return fail(MLA_ERR_INVALID_ARGUMENT, "total must be positive (got %d)", rows);
+  // B * rows < 2^31 for both layouts: the device prefix of the per-sequence
+  // lengths (each clamped to at most `rows`) is int32
+  mla_status s = check_dims(B, rows, H, d, r, dt, cu ? "total" : "Tmax");
+  if (s != MLA_OK) return s;
   if (!std::isfinite(scale)) return fail(MLA_ERR_INVALID_ARGUMENT, "scale must be finite");
   if (!aligned16(q) || !aligned16(kv_latent) || !aligned16(w_up_k) || !aligned16(w_up_v) ||
       !aligned16(out) || !aligned16(workspace) || ((uintptr_t)ints & 3u))
@@ -342,6 +352,18 @@ mla_status mla_decode_varlen_fwd(const void* q, const void* kv_latent, const int
   if (!cu_seqlens) return fail(MLA_ERR_INVALID_ARGUMENT, "null pointer");
   return decode_common(q, kv_latent, nullptr, cu_seqlens, w_up_k, w_up_v, out, B, total, H, d, r, scale, dt,
                        workspace, workspace_bytes, stream);
+}
+
+mla_status mla_decode_set_splits(int splits) {
+  if (splits < 0 || splits > mla::decode_split_cap())
+    return fail(MLA_ERR_INVALID_ARGUMENT, "splits must be in [0, %d] (got %d)", mla::decode_split_cap(), splits);
+  mla::set_decode_splits(splits);
+  return ok();
+}
+
+mla_status mla_set_lds_limit_override(size_t bytes) {
+  g_lds_limit_override.store(bytes, std::memory_order_relaxed);
+  return ok();
 }
 
 mla_status mla_kv_append(void* kv_cache, int32_t* seq_lens, const void* new_latent, int B, int Tmax, int r,

@@ -11,6 +11,9 @@ namespace mla {
 // has at most decode_split_cap() + B - 1 partial slots (workspace sized for it).
 constexpr int decode_split_cap() { return 1024; }
 size_t decode_max_splits(int B);
+// Chunks per head group for later decode calls: 0 = one per compute unit
+// (the default), else 1 .. decode_split_cap() (mla_decode_set_splits).
+void set_decode_splits(int p);
 
 // LDS of the decode split kernel: a ring of four 32-key latent tiles, the
 // probabilities of one tile (2 KB), 64 row maxima and 64 partial sums.

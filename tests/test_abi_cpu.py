@@ -121,6 +121,7 @@ def varlen(**kw):
     ({"B": 0}, mla.MLA_ERR_INVALID_ARGUMENT),
     ({"dt": 5}, mla.MLA_ERR_INVALID_ARGUMENT),
     ({"r": 2048}, mla.MLA_ERR_UNSUPPORTED),
+    ({"B": 4096, "total": 1 << 20}, mla.MLA_ERR_UNSUPPORTED),   # B * total >= 2^31: the length prefix is int32
     ({"wsb": 3}, mla.MLA_ERR_WORKSPACE),
 ])
 def test_varlen_argument_errors(kw, status):
@@ -265,3 +266,44 @@ def test_auto_form_choice():
         mla.mla_latent_attn_unabsorbed_workspace_size(2, 64, 4, 128, 512, BF16)
     assert mla.mla_latent_attn_auto_workspace_size(2, 64, 4, 32, 32, F32) == \
         mla.mla_latent_attn_workspace_size(2, 64, 4, 32, 32, F32)
+
+
+# ---- the LDS-limit check: a device that allows less LDS per block than a
+# kernel needs makes the call fail with MLA_ERR_UNSUPPORTED before anything is
+# enqueued (here on a host without a device: the override replaces the query)
+@pytest.fixture
+def lds_limit():
+    yield mla.mla_set_lds_limit_override
+    mla.mla_set_lds_limit_override(0)
+
+
+def unabs(**kw):
+    a = dict(q=P, kv=P, wk=P, wv=P, out=P, B=2, T=64, H=4, d=128, r=512, scale=0.17, dt=BF16, ws=P, wsb=1 << 40)
+    a.update(kw)
+    return mla.mla_latent_attn_fwd_unabsorbed_raw(a["q"], a["kv"], a["wk"], a["wv"], a["out"], a["B"], a["T"],
+                                                  a["H"], a["d"], a["r"], a["scale"], a["dt"], a["ws"], a["wsb"])
+
+
+@pytest.mark.parametrize("fn", [attn, dec, unabs])
+def test_lds_limit_below_the_kernels_need(fn, lds_limit):
+    lds_limit(64 * 1024)   # well below the 140 KB the r = 512 kernels take
+    assert fn(dt=BF16, d=128, r=512) == mla.MLA_ERR_UNSUPPORTED
+    assert "LDS" in mla.last_error()
+
+
+def test_lds_limit_is_only_checked_for_the_matrix_core_paths(lds_limit):
+    lds_limit(1024)
+    # float32 runs the vector kernels, which need no large LDS tile: the call
+    # gets past the check and fails only at the (absent) device
+    assert attn() == mla.MLA_ERR_HIP
+
+
+def test_decode_split_count_control():
+    try:
+        for bad in (-1, 1025):
+            assert mla.load().mla_decode_set_splits(bad) == mla.MLA_ERR_INVALID_ARGUMENT
+            assert "splits" in mla.last_error()
+        for good in (1, 7, 1024, 0):
+            mla.mla_decode_set_splits(good)
+    finally:
+        mla.mla_decode_set_splits(0)
