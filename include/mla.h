@@ -171,6 +171,27 @@ mla_status mla_decode_fwd(const void* q, const void* kv_latent, const int32_t* s
                           int H, int d, int r, float scale, mla_dtype dt, void* workspace,
                           size_t workspace_bytes, void* stream);
 
+/* Size of the fixed device scratch behind mla_decode_fwd_noalloc (64 MiB). */
+#define MLA_NOALLOC_SCRATCH_BYTES (64u << 20)
+
+/* mla_decode_fwd without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation.  Same arguments (but workspace), same
+ * kernels and the same result, bit for bit, as mla_decode_fwd.  Its scratch
+ * (absorbed queries, W_uv^T, the split's partial states and the length
+ * prefix) lives in a fixed MLA_NOALLOC_SCRATCH_BYTES device array the
+ * library holds on each device until the process ends; the call allocates
+ * nothing and needs no cleared memory.  A shape whose scratch would exceed
+ * it returns MLA_ERR_UNSUPPORTED (bf16_decode's 64 sequences x 32 heads at
+ * r = 512 take about 17 MiB at the default chunk count).  Every call on a
+ * device shares that device's scratch: calls that overlap on one device
+ * (other streams, other threads) race and give wrong results; calls on one
+ * stream are ordered and safe.  The first call on each device looks up the
+ * scratch's device address (a HIP query), so make one before a capture. */
+mla_status mla_decode_fwd_noalloc(const void* q, const void* kv_latent, const int32_t* seq_lens,
+                                  const void* w_up_k, const void* w_up_v, void* out, int B, int Tmax,
+                                  int H, int d, int r, float scale, mla_dtype dt, void* stream);
+
 /* Bytes of workspace mla_decode_varlen_fwd needs for this shape (0 on bad sizes). */
 size_t mla_decode_varlen_workspace_size(int B, int total, int H, int d, int r, mla_dtype dt);
 

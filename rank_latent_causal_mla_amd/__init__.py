@@ -24,7 +24,8 @@ EXPORTED = ("mla_down_proj", "mla_latent_attn_workspace_size", "mla_latent_attn_
             "mla_latent_attn_auto_form", "mla_latent_attn_auto_workspace_size", "mla_latent_attn_fwd_auto",
             "mla_latent_attn_unabsorbed_workspace_size", "mla_latent_attn_fwd_unabsorbed",
             "mla_decode_workspace_size", "mla_decode_fwd", "mla_decode_varlen_workspace_size",
-            "mla_decode_varlen_fwd", "mla_kv_append", "mla_decode_set_splits", "mla_set_lds_limit_override",
+            "mla_decode_fwd_noalloc", "mla_decode_varlen_fwd", "mla_kv_append", "mla_decode_set_splits",
+            "mla_set_lds_limit_override",
             "mla_profile_enable", "mla_profile_collect", "mla_status_string", "mla_last_error")
 
 _lib = None
@@ -84,6 +85,8 @@ def load():
     lib.mla_decode_workspace_size.argtypes = [i32] * 6
     lib.mla_decode_fwd.restype = i32
     lib.mla_decode_fwd.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, i32, vp, sz, vp]
+    lib.mla_decode_fwd_noalloc.restype = i32
+    lib.mla_decode_fwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, i32, vp]
     lib.mla_decode_varlen_workspace_size.restype = sz
     lib.mla_decode_varlen_workspace_size.argtypes = [i32] * 6
     lib.mla_decode_varlen_fwd.restype = i32
@@ -187,6 +190,11 @@ def mla_decode_fwd_raw(q, kv_latent, seq_lens, w_up_k, w_up_v, out, B, Tmax, H, 
                        ws_bytes, stream=0):
     return load().mla_decode_fwd(q, kv_latent, seq_lens, w_up_k, w_up_v, out, B, Tmax, H, d, r, scale, dt, ws,
                                  ws_bytes, stream)
+
+
+def mla_decode_fwd_noalloc_raw(q, kv_latent, seq_lens, w_up_k, w_up_v, out, B, Tmax, H, d, r, scale, dt, stream=0):
+    return load().mla_decode_fwd_noalloc(q, kv_latent, seq_lens, w_up_k, w_up_v, out, B, Tmax, H, d, r, scale, dt,
+                                         stream)
 
 
 def mla_decode_varlen_workspace_size(B, total, H, d, r, dt):
@@ -450,6 +458,27 @@ def mla_decode_fwd(q, kv_latent, seq_lens, w_up_k, w_up_v, out=None, scale=None,
                               w_up_v.data_ptr(), out.data_ptr(), B, Tmax, H, d, r, float(scale), dt,
                               workspace.data_ptr(), workspace.numel() * workspace.element_size(),
                               _stream(stream)))
+    return out
+
+
+def mla_decode_fwd_noalloc(q, kv_latent, seq_lens, w_up_k, w_up_v, out, scale=None, stream=None):
+    """mla_decode_fwd on the library's fixed device scratch: no workspace and no
+    allocation (the caller passes `out`, [B,1,H,d] in q's dtype)."""
+    if kv_latent.dim() != 3:
+        raise ValueError(f"kv_latent must be [B, Tmax, r], got {list(kv_latent.shape)}")
+    B, Tmax, r = kv_latent.shape
+    Bq, H, d = _decode_dims(q, w_up_k, w_up_v, r)
+    if Bq != B:
+        raise ValueError(f"q must be [B={B}, 1, H, d] like kv_latent, got {list(q.shape)}")
+    _int32_vec(seq_lens, B, "seq_lens")
+    _same_float(("q", q), ("kv_latent", kv_latent), ("w_up_k", w_up_k), ("w_up_v", w_up_v))
+    _shaped(out, q.shape, q.dtype, "out")
+    _dev(q, kv_latent, seq_lens, w_up_k, w_up_v, out)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    _check(mla_decode_fwd_noalloc_raw(q.data_ptr(), kv_latent.data_ptr(), seq_lens.data_ptr(), w_up_k.data_ptr(),
+                                      w_up_v.data_ptr(), out.data_ptr(), B, Tmax, H, d, r, float(scale), _dt(q),
+                                      _stream(stream)))
     return out
 
 

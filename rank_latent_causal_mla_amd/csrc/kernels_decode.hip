@@ -10,6 +10,8 @@
 //                       block writes one partial state per head;
 //   decode_merge_up  -- log-sum-exp merge of the partial states of each
 //                       (b, h), then the W_uv up-projection on the matrix unit.
+#include <algorithm>
+
 #include "mla_device.h"
 #include "mla_kernels.h"
 #include "host_once.h"
@@ -476,17 +478,21 @@ void set_decode_splits(int p) { g_decode_splits.store(p, std::memory_order_relax
 
 size_t decode_max_splits(int B) { return (size_t)decode_split_cap() + B; }
 
-template <int R>
-static hipError_t run_decode(const uint16_t* q, const uint16_t* lat, const int32_t* lens, const int32_t* cu,
-                             const uint16_t* wk, const uint16_t* wv, uint16_t* out, int B, int Tmax,
-                             int H, int d, float sl2, uint16_t* q_lat, uint16_t* part_o, float* part_ml,
-                             uint16_t* wvT, int32_t* S, int32_t* RB, hipStream_t st) {
+int decode_chunks(int H) {
   // one chunk of keys per compute unit over all head groups (or the count set
   // by mla_decode_set_splits)
   const int nhg = (H + 31) / 32;
   const int forced = decode_splits_override();
-  int P = forced > 0 ? forced : device_cus() / nhg;
-  P = P < 1 ? 1 : (P > decode_split_cap() ? decode_split_cap() : P);
+  const int P = forced > 0 ? forced : device_cus() / nhg;
+  return P < 1 ? 1 : (P > decode_split_cap() ? decode_split_cap() : P);
+}
+
+template <int R>
+static hipError_t run_decode(const uint16_t* q, const uint16_t* lat, const int32_t* lens, const int32_t* cu,
+                             const uint16_t* wk, const uint16_t* wv, uint16_t* out, int B, int Tmax,
+                             int H, int d, float sl2, uint16_t* q_lat, uint16_t* part_o, float* part_ml,
+                             uint16_t* wvT, int32_t* S, int32_t* RB, int P, hipStream_t st) {
+  const int nhg = (H + 31) / 32;
   const size_t lds = decode_lds_bytes(R);
   static OnceFlag attrs;
   const hipError_t e = run_once(attrs, [lds] {
@@ -525,12 +531,12 @@ static hipError_t run_decode(const uint16_t* q, const uint16_t* lat, const int32
 
 // Workspace: q_lat [B*H][r] bf16 | W_uv^T [H][d][r] | partial o [M][H][r] bf16 |
 // partial (m, l) [M][H][2] f32 | length prefix [B + 1] int32 | row bases [B] int32, with
-// M = decode_split_cap() + B partial slots; each part 256-byte aligned.
+// M partial slots (chunk g of sequence b writes slot g + b, so M >= chunks + B);
+// each part 256-byte aligned.
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-size_t decode_mfma_workspace(int B, int Tmax, int H, int d, int r) {
-  (void)Tmax;
-  const size_t M = decode_max_splits(B);
+size_t decode_mfma_bytes(int B, int H, int d, int r, size_t slots) {
+  const size_t M = slots;
   size_t bytes = align256((size_t)B * H * r * 2);
   bytes = align256(bytes + (size_t)H * d * r * 2);
   bytes = align256(bytes + M * H * r * 2);
@@ -539,10 +545,17 @@ size_t decode_mfma_workspace(int B, int Tmax, int H, int d, int r) {
   return bytes;
 }
 
+size_t decode_mfma_workspace(int B, int Tmax, int H, int d, int r) {
+  (void)Tmax;
+  return decode_mfma_bytes(B, H, d, r, decode_max_splits(B));
+}
+
 hipError_t decode_mfma(const void* q, const void* lat, const int32_t* lens, const int32_t* cu, const void* wk,
                        const void* wv, void* out, int B, int Tmax, int H, int d, int r, float sl2,
-                       void* ws, hipStream_t st) {
-  const size_t M = decode_max_splits(B);
+                       void* ws, size_t slots, hipStream_t st) {
+  const size_t M = slots;
+  // chunks per head group, within the slots the workspace was laid out for
+  const int P = (int)std::min<size_t>((size_t)decode_chunks(H), slots - (size_t)B);
   char* p = (char*)ws;
   uint16_t* q_lat = (uint16_t*)p;
   size_t off = align256((size_t)B * H * r * 2);
@@ -555,7 +568,7 @@ hipError_t decode_mfma(const void* q, const void* lat, const int32_t* lens, cons
   int32_t* S = (int32_t*)(p + off);
   int32_t* RB = S + B + 1;
 #define ARGS (const uint16_t*)q, (const uint16_t*)lat, lens, cu, (const uint16_t*)wk, (const uint16_t*)wv, \
-             (uint16_t*)out, B, Tmax, H, d, sl2, q_lat, part_o, part_ml, wvT, S, RB, st
+             (uint16_t*)out, B, Tmax, H, d, sl2, q_lat, part_o, part_ml, wvT, S, RB, P, st
   switch (r) {
     case 128: return run_decode<128>(ARGS);
     case 256: return run_decode<256>(ARGS);

@@ -4,6 +4,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <string>
 
 #include "../../include/mla.h"
@@ -289,14 +290,46 @@ size_t mla_decode_workspace_size(int B, int Tmax, int H, int d, int r, mla_dtype
 
 }  // extern "C"
 
+// The fixed decode scratch of mla_decode_fwd_noalloc: device memory the
+// library holds from load to process end (one copy per device, at its own
+// address), so that call allocates nothing.  Host code never uses this name
+// as an address: it is a host-side stand-in; the device address comes from
+// hipGetSymbolAddress, once per device (scratch_address below).
+static __device__ __align__(256) unsigned char scratch[MLA_NOALLOC_SCRATCH_BYTES];
+
 namespace {
 
+// The device address of `scratch` on the calling thread's current device,
+// looked up on the first call on each device and kept.
+mla_status scratch_address(void** ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(MLA_ERR_HIP, "device query failed: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(MLA_ERR_UNSUPPORTED, "device %d beyond %d devices", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(MLA_ERR_HIP, "scratch address lookup failed: %s", hipGetErrorString(e));
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return MLA_OK;
+}
+
 // Decode over a padded cache (lens, rows = Tmax per sequence) or a packed one
-// (cu, rows = the cache's total row count).
+// (cu, rows = the cache's total row count).  With `noalloc` the workspace is
+// the library's fixed scratch (workspace and workspace_bytes are ignored),
+// laid out with the partial slots this call's chunk count needs.
 mla_status decode_common(const void* q, const void* kv_latent, const int32_t* seq_lens, const int32_t* cu,
                          const void* w_up_k, const void* w_up_v, void* out, int B, int rows, int H, int d, int r,
-                         float scale, mla_dtype dt, void* workspace, size_t workspace_bytes, void* stream) {
-  if (!q || !kv_latent || !(seq_lens || cu) || !w_up_k || !w_up_v || !out || !workspace)
+                         float scale, mla_dtype dt, void* workspace, size_t workspace_bytes, void* stream,
+                         bool noalloc = false) {
+  if (!q || !kv_latent || !(seq_lens || cu) || !w_up_k || !w_up_v || !out || !(workspace || noalloc))
     return fail(MLA_ERR_INVALID_ARGUMENT, "null pointer");
   const int32_t* ints = cu ? cu : seq_lens;
   if (cu && rows < 1) return fail(MLA_ERR_INVALID_ARGUMENT, "total must be positive (got %d)", rows);
@@ -306,11 +339,23 @@ mla_status decode_common(const void* q, const void* kv_latent, const int32_t* se
   if (s != MLA_OK) return s;
   if (!std::isfinite(scale)) return fail(MLA_ERR_INVALID_ARGUMENT, "scale must be finite");
   if (!aligned16(q) || !aligned16(kv_latent) || !aligned16(w_up_k) || !aligned16(w_up_v) ||
-      !aligned16(out) || !aligned16(workspace) || ((uintptr_t)ints & 3u))
+      !aligned16(out) || (!noalloc && !aligned16(workspace)) || ((uintptr_t)ints & 3u))
     return fail(MLA_ERR_INVALID_ARGUMENT, "pointers must be 16-byte aligned (lengths 4-byte)");
-  const size_t need = mla_decode_workspace_size(B, rows, H, d, r, dt);
-  if (workspace_bytes < need)
-    return fail(MLA_ERR_WORKSPACE, "workspace %zu bytes < %zu required", workspace_bytes, need);
+  // partial slots of the matrix-core path: the caller's workspace is sized
+  // for the most chunks a call can take, the fixed scratch for this call's
+  size_t slots = mla::decode_max_splits(B);
+  if (noalloc) {
+    slots = (size_t)mla::decode_chunks(H) + B;
+    const size_t need = use_mfma(dt, d, r) ? mla::decode_mfma_bytes(B, H, d, r, slots)
+                                           : mla::decode_simt_workspace(B, rows, H, d, r);
+    if (need > MLA_NOALLOC_SCRATCH_BYTES)
+      return fail(MLA_ERR_UNSUPPORTED, "decode needs %zu bytes of scratch; the fixed scratch holds %zu", need,
+                  (size_t)MLA_NOALLOC_SCRATCH_BYTES);
+  } else {
+    const size_t need = mla_decode_workspace_size(B, rows, H, d, r, dt);
+    if (workspace_bytes < need)
+      return fail(MLA_ERR_WORKSPACE, "workspace %zu bytes < %zu required", workspace_bytes, need);
+  }
   hipStream_t st = (hipStream_t)stream;
   if (use_mfma(dt, d, r)) {
     size_t limit = 0;
@@ -319,8 +364,14 @@ mla_status decode_common(const void* q, const void* kv_latent, const int32_t* se
     if (mla::decode_lds_bytes(r) > limit)
       return fail(MLA_ERR_UNSUPPORTED, "decode needs %zu bytes of LDS per block, device allows %zu",
                   mla::decode_lds_bytes(r), limit);
+  }
+  if (noalloc) {
+    s = scratch_address(&workspace);
+    if (s != MLA_OK) return s;
+  }
+  if (use_mfma(dt, d, r)) {
     return launched(mla::decode_mfma(q, kv_latent, seq_lens, cu, w_up_k, w_up_v, out, B, rows, H, d, r,
-                                     (float)(scale * kLog2e), workspace, st),
+                                     (float)(scale * kLog2e), workspace, slots, st),
                     "decode launch");
   }
   return launched(mla::decode_simt(dt == MLA_DTYPE_BF16, q, kv_latent, seq_lens, cu, w_up_k, w_up_v,
@@ -339,6 +390,14 @@ mla_status mla_decode_fwd(const void* q, const void* kv_latent, const int32_t* s
   if (!seq_lens) return fail(MLA_ERR_INVALID_ARGUMENT, "null pointer");
   return decode_common(q, kv_latent, seq_lens, nullptr, w_up_k, w_up_v, out, B, Tmax, H, d, r, scale, dt,
                        workspace, workspace_bytes, stream);
+}
+
+mla_status mla_decode_fwd_noalloc(const void* q, const void* kv_latent, const int32_t* seq_lens, const void* w_up_k,
+                                  const void* w_up_v, void* out, int B, int Tmax, int H, int d, int r, float scale,
+                                  mla_dtype dt, void* stream) {
+  if (!seq_lens) return fail(MLA_ERR_INVALID_ARGUMENT, "null pointer");
+  return decode_common(q, kv_latent, seq_lens, nullptr, w_up_k, w_up_v, out, B, Tmax, H, d, r, scale, dt, nullptr,
+                       0, stream, /*noalloc=*/true);
 }
 
 size_t mla_decode_varlen_workspace_size(int B, int total, int H, int d, int r, mla_dtype dt) {

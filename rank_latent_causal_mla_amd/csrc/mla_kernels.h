@@ -35,10 +35,15 @@ hipError_t prefill_mfma(const void* q, const void* lat, const void* wk, const vo
 size_t prefill_mfma_workspace(int B, int T, int H, int d, int r);
 size_t key_mask_workspace(int B, int T, int r);
 size_t decode_mfma_workspace(int B, int Tmax, int H, int d, int r);
-// lens (padded cache [B, Tmax, r]) or cu (packed cache [Tmax = total rows, r]; lens unused)
+// Decode workspace bytes with `slots` partial slots (>= decode_chunks(H) + B).
+size_t decode_mfma_bytes(int B, int H, int d, int r, size_t slots);
+// Chunks per head group the decode split takes (the CU count, or mla_decode_set_splits).
+int decode_chunks(int H);
+// lens (padded cache [B, Tmax, r]) or cu (packed cache [Tmax = total rows, r]; lens unused); ws laid out
+// with `slots` partial slots (decode_mfma_bytes)
 hipError_t decode_mfma(const void* q, const void* lat, const int32_t* lens, const int32_t* cu, const void* wk,
                        const void* wv, void* out, int B, int Tmax, int H, int d, int r, float sl2,
-                       void* ws, hipStream_t st);
+                       void* ws, size_t slots, hipStream_t st);
 // q_lat[n*H + h, :] = qscale * W_uk[:, h, :] q[n, h, :] for N tokens (bf16).
 hipError_t absorb_mfma(const uint16_t* q, const uint16_t* wk, uint16_t* q_lat, int N, int H, int d,
                        int R, float qscale, hipStream_t st);
