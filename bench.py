@@ -127,8 +127,22 @@ def prefill_row_flops(cfg, t: int) -> int:
     return 2 * cfg.d * cfg.r + 4 * cfg.r * (t + 1) + 2 * cfg.r * cfg.d
 
 
+def to_device(arr):
+    """A stored input array (float32, or uint16 bf16 bit patterns) -> a device tensor."""
+    import torch
+    if arr.dtype == np.uint16:
+        return torch.from_numpy(arr.view(np.int16).copy()).cuda().view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(arr)).cuda()
+
+
 # ---------------------------------------------------------------- GPU timing
+MIN_TIMED_CALLS = 50   # calls timed one by one for the median and minimum
+
+
 def time_steps(fn, steps: int, warmup: int):
+    """Mean ms per call over `steps` calls between two synchronisations (the
+    headline figure), then the median and minimum of max(steps, 50) calls
+    each bracketed by its own pair of events on the current stream."""
     import torch
     for _ in range(warmup):
         fn(0)
@@ -139,7 +153,16 @@ def time_steps(fn, steps: int, warmup: int):
         fn(i)
     e1.record()
     torch.cuda.synchronize()
-    return e0.elapsed_time(e1) / steps
+    mean = e0.elapsed_time(e1) / steps
+    n = max(steps, MIN_TIMED_CALLS)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    for i, (a, b) in enumerate(ev):
+        a.record()
+        fn(i)
+        b.record()
+    torch.cuda.synchronize()
+    each = sorted(a.elapsed_time(b) for a, b in ev)
+    return mean, {"median_ms": round(float(np.median(each)), 4), "min_ms": round(each[0], 4), "calls": n}
 
 
 def kernel_times(fn, steps: int):
@@ -161,7 +184,6 @@ def bench_prefill(cfg, steps, warmup, unabsorbed=False, masked=False):
     import torch
     import synth
     import rank_latent_causal_mla_amd as mla
-    from tests.helpers import to_device
     inp = synth.make_inputs(cfg)
     dev = {k: to_device(v) for k, v in inp.items()}
     out = torch.empty_like(dev["q"])
@@ -182,9 +204,9 @@ def bench_prefill(cfg, steps, warmup, unabsorbed=False, masked=False):
         else:
             fwd(dev["q"], dev["kv_latent"], dev["w_up_k"], dev["w_up_v"], out=out, scale=cfg.scale, workspace=ws)
 
-    ms = time_steps(step, steps, warmup)
+    ms, dist = time_steps(step, steps, warmup)
     kt = kernel_times(step, steps)
-    return ms, kt, inp
+    return ms, kt, inp, dist
 
 
 def bench_full(cfg, steps, warmup):
@@ -193,7 +215,6 @@ def bench_full(cfg, steps, warmup):
     import torch
     import synth
     import rank_latent_causal_mla_amd as mla
-    from tests.helpers import to_device
     inp = synth.make_inputs(cfg)
     dev = {k: to_device(v) for k, v in inp.items()}
     out = torch.empty_like(dev["q"])
@@ -206,7 +227,8 @@ def bench_full(cfg, steps, warmup):
         mla.mla_latent_attn_fwd_full(dev["hidden"], dev["w_down"], dev["q"], dev["w_up_k"], dev["w_up_v"],
                                      kv_latent=lat, out=out, scale=cfg.scale, workspace=ws)
 
-    return time_steps(step, steps, warmup), kernel_times(step, steps)
+    ms, dist = time_steps(step, steps, warmup)
+    return ms, kernel_times(step, steps), dist
 
 
 def bench_decode_varlen(cfg, steps, warmup, copies=3):
@@ -214,7 +236,6 @@ def bench_decode_varlen(cfg, steps, warmup, copies=3):
     import torch
     import synth
     import rank_latent_causal_mla_amd as mla
-    from tests.helpers import to_device
     inp = synth.make_inputs(cfg)
     lens = inp["seq_lens"]
     dev = {k: to_device(v) for k, v in inp.items() if k not in ("seq_lens", "kv_latent")}
@@ -239,7 +260,6 @@ def bench_decode(cfg, steps, warmup, copies=3):
     import torch
     import synth
     import rank_latent_causal_mla_amd as mla
-    from tests.helpers import to_device
     inp = synth.make_inputs(cfg)
     lens = inp["seq_lens"]
     dev = {k: to_device(v) for k, v in inp.items() if k != "seq_lens"}
@@ -254,32 +274,101 @@ def bench_decode(cfg, steps, warmup, copies=3):
         mla.mla_decode_fwd(dev["q"], caches[i % copies], dlens, dev["w_up_k"], dev["w_up_v"], out=out,
                            scale=cfg.scale, workspace=ws)
 
-    ms = time_steps(step, steps, warmup)
+    ms, dist = time_steps(step, steps, warmup)
     kt = kernel_times(step, steps)
-    return ms, kt, lens
+    return ms, kt, lens, dist
 
 
 # ---------------------------------------------------------------- CPU baseline
-def cpu_baseline(cfg, inp, n_heads=16, n_rows=64):
-    """The fp64 oracle on a bounded sample of the prefill workload: n_rows query
-    positions spread evenly over 0..T-1 for each of n_heads heads of batch 0."""
+def host_info() -> dict:
+    """The host the oracle runs on: CPU model, logical CPUs, the CPUs this
+    process may run on, and the threads the oracle starts by default."""
+    import platform
     import oracle
-    heads = list(range(min(n_heads, cfg.H)))
-    ts = [int(x) for x in np.linspace(0, cfg.T - 1, n_rows).round()]
-    rb = np.zeros(len(heads) * len(ts), dtype=np.int64)
-    rh = np.repeat(heads, len(ts))
-    rt = np.tile(ts, len(heads))
-    qrows = inp["q"][rb, rt, rh]
-    threads = oracle.threads(0)
-    t0 = time.perf_counter()
-    oracle.attend_rows(qrows, rb, rh, rt + 1, inp["kv_latent"], inp["w_up_k"], inp["w_up_v"], cfg.scale)
-    sec = time.perf_counter() - t0
-    flops = sum(prefill_row_flops(cfg, int(t)) for t in rt)
-    return {"value": flops / sec / 1e12, "unit": "TFLOP/s", "cores": min(threads, len(heads)),
-            "kind": "oracle", "seconds": round(sec, 3),
-            "sample": f"{len(rt)} query rows of {cfg.name}: {len(ts)} positions evenly spaced over 0..{cfg.T - 1} "
-                      f"for heads 0..{len(heads) - 1} of batch 0 (the oracle materialises k, v for the "
-                      f"{cfg.T} keys of each head); value = absorbed-method FLOPs of those rows / wall time"}
+    model = platform.processor() or ""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        allowed = sorted(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        allowed = []
+    return {"cpu_model": model, "logical_cpus": os.cpu_count(), "affinity_cpus": len(allowed),
+            "affinity": f"{allowed[0]}-{allowed[-1]}" if allowed and allowed[-1] - allowed[0] + 1 == len(allowed)
+            else ",".join(map(str, allowed)), "oracle_threads": oracle.threads(0)}
+
+
+def oracle_flops(groups: dict, rows_nkeys, d: int, r: int) -> int:
+    """FLOPs the oracle itself executes: for each (b, h) group, k and v of its
+    nk keys (2 products of 2 r d each per key), then per row of n keys the
+    logits and the weighted sum of v (2 d each per key)."""
+    return sum(4 * nk * d * r for nk in groups.values()) + sum(4 * d * int(n) for n in rows_nkeys)
+
+
+def cpu_baseline(work):
+    """The fp64 oracle, as it stands, on bounded samples of the three bf16
+    workloads; each sample attends the given rows over their full causal
+    key range, so the oracle materialises k and v for every key of each
+    sampled (b, h) pair."""
+    import oracle
+    samples, tot_abs, tot_orc, tot_sec = [], 0, 0, 0.0
+    for name, cfg, inp, rb, rh, nkeys, qrows, abs_flops in work:
+        groups = {}
+        for b, h, n in zip(rb, rh, nkeys):
+            groups[(int(b), int(h))] = max(groups.get((int(b), int(h)), 0), int(n))
+        t0 = time.perf_counter()
+        oracle.attend_rows(qrows, rb, rh, nkeys, inp["kv_latent"], inp["w_up_k"], inp["w_up_v"], cfg.scale)
+        sec = time.perf_counter() - t0
+        of = oracle_flops(groups, nkeys, cfg.d, cfg.r)
+        samples.append({"workload": name, "rows": len(rb), "bh_pairs": len(groups), "seconds": round(sec, 3),
+                        "absorbed_tflops": round(abs_flops / sec / 1e12, 6), "oracle_tflops": round(of / sec / 1e12, 6),
+                        "threads_used": min(oracle.threads(0), len(groups))})
+        tot_abs += abs_flops
+        tot_orc += of
+        tot_sec += sec
+    info = host_info()
+    first = samples[0]
+    return {"value": first["absorbed_tflops"], "unit": "TFLOP/s", "cores": first["threads_used"], "kind": "oracle",
+            "sample": "; ".join(f"{x['workload']}: {x['rows']} query rows over {x['bh_pairs']} (b, h) pairs, "
+                                f"each over its full causal key range ({x['seconds']} s)" for x in samples),
+            "what": "value: absorbed-method FLOPs of the sampled rows of the headline workload per second of the "
+                    "oracle's wall time; oracle_tflops: the FLOPs the oracle itself executes (k and v materialised "
+                    "for every key of each sampled (b, h) pair, then d-wide products) per second",
+            "oracle_tflops": first["oracle_tflops"], "seconds": round(tot_sec, 3), "samples": samples, **info}
+
+
+def cpu_work(cfg, inp, dcfg):
+    """The bounded samples the CPU baseline times: the headline prefill workload
+    (8 heads of batch 0, 48 positions spread over the sequence), bf16_prefill
+    (16 (b, h) pairs, 32 positions each) and bf16_decode (4 sequences x 8 heads)."""
+    import synth
+    work = []
+    prefills = [(cfg, inp, [(0, h) for h in range(min(8, cfg.H))], 48)]
+    if cfg.name != "bf16_prefill":
+        c3 = synth.CONFIGS["bf16_prefill"]
+        prefills.append((c3, synth.make_inputs(c3), [(b, h) for b in range(0, 8, 2) for h in range(0, 16, 4)], 32))
+    for c, ci, heads, npos in prefills:
+        ts = [int(x) for x in np.linspace(0, c.T - 1, npos).round()]
+        rb = np.repeat([b for b, _ in heads], len(ts))
+        rh = np.repeat([h for _, h in heads], len(ts))
+        rt = np.tile(ts, len(heads))
+        flops = sum(prefill_row_flops(c, int(t)) for t in rt)
+        work.append((c.name, c, ci, rb, rh, rt + 1, ci["q"][rb, rt, rh], flops))
+    if dcfg is not None:
+        di = synth.make_inputs(dcfg)
+        lens = di["seq_lens"]
+        seqs = [int(x) for x in np.argsort(lens, kind="stable")[::16][:4]]   # four sequences across the length range
+        rb = np.repeat(seqs, 8)
+        rh = np.tile(np.arange(8), len(seqs))
+        nk = lens[rb]
+        flops = sum(2 * dcfg.d * dcfg.r + 4 * dcfg.r * int(n) + 2 * dcfg.r * dcfg.d for n in nk)
+        work.append((dcfg.name, dcfg, di, rb, rh, nk, di["q"][rb, 0, rh], flops))
+    return work
 
 
 def main(argv=None):
@@ -320,7 +409,10 @@ def main(argv=None):
         del src, dst
 
     cfg = synth.CONFIGS[args.workload]
-    ms, kt, inp = bench_prefill(cfg, args.steps, args.warmup)
+    ms, kt, inp, dist = bench_prefill(cfg, args.steps, args.warmup)
+    # the shorter workloads below (calls of 0.1-1 ms) get at least 20 warm-up
+    # calls, so that the clocks have settled when their timing starts
+    sub_warmup = max(args.warmup, 20)
     work = prefill_flops(cfg)
     value = work["total"] / (ms * 1e-3) / 1e12
     flash = kt.get("flash_latent_bf16")
@@ -340,19 +432,21 @@ def main(argv=None):
         "config": {"workload": cfg.name, "B": cfg.B, "T": cfg.T, "H": cfg.H, "d": cfg.d, "r": cfg.r,
                    "causal": True, "flops_per_step": work["total"]},
         "roofline": roof,
+        "per_call": dist,
         "kernels_ms": {k: round(v["avg_ms"], 4) for k, v in kt.items()},
     }
     if args.workload == "bf16_long_prefill" and not args.no_short:
         # the shorter bf16 prefill workload (B=8, T=2048, H=16): the same kernels at a length where each query
         # block carries 8x less work, so fixed costs per block weigh more
         scfg = synth.CONFIGS["bf16_prefill"]
-        sms, skt, _ = bench_prefill(scfg, args.steps, args.warmup)
+        sms, skt, _, sdist = bench_prefill(scfg, args.steps, sub_warmup)
         sw = prefill_flops(scfg)
         sfl = skt.get("flash_latent_bf16")
-        ums_s, _, _ = bench_prefill(scfg, args.steps, args.warmup, unabsorbed=True)
+        ums_s, _, _, _ = bench_prefill(scfg, args.steps, sub_warmup, unabsorbed=True)
         line["prefill_short"] = {
             "workload": scfg.name, "value": round(sw["total"] / (sms * 1e-3) / 1e12, 2), "unit": "TFLOP/s",
-            "ms_per_step": round(sms, 4), "flops_per_step": sw["total"], "unabsorbed_ms_per_step": round(ums_s, 4),
+            "ms_per_step": round(sms, 4), "per_call": sdist, "flops_per_step": sw["total"],
+            "unabsorbed_ms_per_step": round(ums_s, 4),
             "roofline": None if not sfl else {
                 "bound": "mfma", "achieved": round(sw["attn"] / (sfl["avg_ms"] * 1e-3) / 1e12, 2),
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
@@ -361,7 +455,7 @@ def main(argv=None):
             "kernels_ms": {k: round(v["avg_ms"], 4) for k, v in skt.items()}}
     if not args.no_unabsorbed and cfg.dtype == "bf16" and \
             mla.mla_latent_attn_unabsorbed_workspace_size(cfg.B, cfg.T, cfg.H, cfg.d, cfg.r, mla.MLA_DTYPE_BF16):
-        ums, ukt, _ = bench_prefill(cfg, args.steps, args.warmup, unabsorbed=True)
+        ums, ukt, _, udist = bench_prefill(cfg, args.steps, args.warmup, unabsorbed=True)
         uw = unabsorbed_flops(cfg)
         mha = ukt.get("flash_mha_bf16")
         uroof = None
@@ -374,10 +468,11 @@ def main(argv=None):
             "what": "the same prefill with k and v materialised (mla_latent_attn_fwd_unabsorbed); value counts "
                     "that form's own FLOPs",
             "value": round(uw["total"] / (ums * 1e-3) / 1e12, 2), "unit": "TFLOP/s", "ms_per_step": round(ums, 4),
+            "per_call": udist,
             "flops_per_step": uw["total"], "step_time_vs_absorbed": round(ms / ums, 3), "roofline": uroof,
             "kernels_ms": {k: round(v["avg_ms"], 4) for k, v in ukt.items()}}
     if not args.no_masked:
-        mms, mkt, minp = bench_prefill(cfg, args.steps, args.warmup, masked=True)
+        mms, mkt, minp, mdist = bench_prefill(cfg, args.steps, args.warmup, masked=True)
         mw = masked_flops(cfg, minp["key_mask"])
         mflash = mkt.get("flash_latent_bf16_masked")
         line["masked"] = {
@@ -385,7 +480,7 @@ def main(argv=None):
                     "length uniform on [T/2, T] and 5% of the rest masked; the visible keys are packed first and "
                     "masked keys are skipped; value counts the visible causal keys only",
             "value": round(mw["total"] / (mms * 1e-3) / 1e12, 2), "unit": "TFLOP/s",
-            "ms_per_step": round(mms, 4), "flops_per_step": mw["total"],
+            "ms_per_step": round(mms, 4), "per_call": mdist, "flops_per_step": mw["total"],
             "roofline": None if not mflash else {
                 "bound": "mfma", "achieved": round(mw["attn"] / (mflash["avg_ms"] * 1e-3) / 1e12, 2),
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
@@ -399,7 +494,7 @@ def main(argv=None):
         line["full_path"] = []
         for fcfg in (synth.CONFIGS["fp32_full_path"],
                      dataclasses.replace(synth.CONFIGS["bf16_prefill"], name="bf16_prefill_down1024", D=1024)):
-            fms, fkt = bench_full(fcfg, args.steps, args.warmup)
+            fms, fkt, fdist = bench_full(fcfg, args.steps, sub_warmup)
             fw = prefill_flops(fcfg)
             down = fkt.get("down_bf16") or fkt.get("down_f32")
             if fcfg.dtype == "bf16":
@@ -420,13 +515,13 @@ def main(argv=None):
                 "workload": fcfg.name, "dtype": fcfg.dtype,
                 "shape": {"B": fcfg.B, "T": fcfg.T, "D": fcfg.D, "H": fcfg.H, "d": fcfg.d, "r": fcfg.r},
                 "value": round(fw["total"] / (fms * 1e-3) / 1e12, 2), "unit": "TFLOP/s",
-                "ms_per_step": round(fms, 4), "flops_per_step": fw["total"],
+                "ms_per_step": round(fms, 4), "per_call": fdist, "flops_per_step": fw["total"],
                 "down_tflops": round(fw["down"] / (down["avg_ms"] * 1e-3) / 1e12, 2) if down else None,
                 "roofline": froof,
                 "kernels_ms": {k: round(v["avg_ms"], 4) for k, v in fkt.items()}})
     if not args.no_decode:
         dcfg = synth.CONFIGS[args.decode_workload]
-        dms, dkt, lens = bench_decode(dcfg, max(args.steps, 10), args.warmup)
+        dms, dkt, lens, ddist = bench_decode(dcfg, max(args.steps, 10), sub_warmup)
         db = decode_bytes(dcfg, lens)
         split = dkt.get("decode_split")
         droof = None
@@ -437,16 +532,19 @@ def main(argv=None):
                      "kernel": "decode_split",
                      "avg_ms": round(split["avg_ms"], 4), "bytes_per_launch": db["latent"]}
         line["decode"] = {"workload": dcfg.name, "value": round(db["total"] / (dms * 1e-3) / 1e9, 1),
-                          "unit": "GB/s", "ms_per_step": round(dms, 4), "bytes_per_step": db["total"],
+                          "unit": "GB/s", "ms_per_step": round(dms, 4), "per_call": ddist,
+                          "bytes_per_step": db["total"],
                           "sum_seq_lens": int(np.sum(lens)), "roofline": droof,
                           "kernels_ms": {k: round(v["avg_ms"], 4) for k, v in dkt.items()}}
         if dcfg.dtype == "bf16":
-            vms = bench_decode_varlen(dcfg, max(args.steps, 10), args.warmup)
+            vms, vdist = bench_decode_varlen(dcfg, max(args.steps, 10), sub_warmup)
             line["decode"]["varlen"] = {"what": "the same decode over a packed cache (mla_decode_varlen_fwd)",
                                         "value": round(db["total"] / (vms * 1e-3) / 1e9, 1), "unit": "GB/s",
-                                        "ms_per_step": round(vms, 4)}
+                                        "ms_per_step": round(vms, 4), "per_call": vdist}
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(cfg, inp)
+        import synth as _synth
+        line["cpu_baseline"] = cpu_baseline(cpu_work(cfg, inp, None if args.no_decode
+                                                     else _synth.CONFIGS[args.decode_workload]))
     print(json.dumps(line), flush=True)
     return 0
 
