@@ -6,17 +6,17 @@
 // header, table or helper with the HIP library.
 //
 // Definition followed (POPCORNBENCH page FW-GLM-5-1 l2_p31, the latent
-// attention problem: its restatement of the reference model's algorithm):
-//   for each batch b, head h and query position t, and every key position
-//   s = 0 .. t (inclusive, causal):
-//     latent = kv_latent[b, s]            (r values)
-//     k      = latent @ w_up_k[:, h]      (d values; w_up_k laid out [r, H, d])
-//     v      = latent @ w_up_v[:, h]
-//     logit  = (q[b, t, h] * k).sum() * scale
-//   softmax over the logits of s = 0 .. t (max-subtracted: find the max,
-//   sum the exponentials, divide -- the three passes the same page spells
-//   out), then the probability-weighted sum of the v vectors.
-// k and v are materialised explicitly, once per (b, h), exactly as defined.
+// attention problem, its restatement of the reference model's algorithm),
+// in this file's notation: for batch b, head h and query position t, the
+// keys are the positions s with 0 <= s <= t (causal, inclusive), and
+//   K_s[e]  = sum_rho L[b,s,rho] * Wk[rho,h,e],   V_s[e] = sum_rho L[b,s,rho] * Wv[rho,h,e]
+//   z_s     = scale * sum_e Q[b,t,h,e] * K_s[e]
+//   p_s     = exp(z_s - max_s z) / sum_s' exp(z_s' - max_s z)
+//   O[b,t,h,e] = sum_s p_s * V_s[e]
+// with L = kv_latent [B,T,r], Wk = w_up_k and Wv = w_up_v [r,H,d], Q = q
+// [B,T,H,d].  The softmax is taken in the page's three passes (the maximum,
+// the sum of the exponentials, the division).  K and V are materialised
+// explicitly, once per (b, h).
 //
 // Down-projection (POPCORNBENCH page FW-GLM-5-1 l2_p1, the KV compression
 // problem: its list of shapes and operations): latent = hidden @ w_down with
