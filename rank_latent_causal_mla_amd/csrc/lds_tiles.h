@@ -74,9 +74,10 @@ __device__ __forceinline__ void dma_tile32(const uint16_t* latb, int k0, int ken
   constexpr int RPI = 64 / NC;  // key rows per instruction
   constexpr int NI = kTileKeys * R * 2 / 1024 / 4;  // instructions per wave
   static_assert(NC <= 64 && 64 % NC == 0, "a copy instruction covers whole rows");
-  int lane = threadIdx.x & 63;
+  unsigned lane = threadIdx.x & 63;
   if (REMAT) asm volatile("" : "+v"(lane));
-  const int sl = lane / NC, p = lane % NC;
+  // with one row per instruction (R = 512) the row is wave-uniform
+  const int sl = RPI == 1 ? 0 : (int)(lane / NC), p = (int)(lane % NC);
 #pragma unroll
   for (int i = 0; i < NI; ++i) {
     const int ins = 4 * i + w;       // wave-uniform
