@@ -345,11 +345,13 @@ struct Flash {
   // current one (scores sc) spread over its matrix ops: the update is cut
   // into 40 pieces of a few vector instructions, and piece k is issued after
   // matrix op k + kPieceLag, so it runs while the matrix unit is busy instead
-  // of between the two products.  Scores are in log2 units (q_lat carries
+  // of between the two products.  At R = 512 the pieces fill the last 40 of
+  // the 64 matrix ops (a lag of 24 ran 1% faster than 8; 12, 16, 18 and 22
+  // were no better than 8).  Scores are in log2 units (q_lat carries
   // scale * log2 e).  With MASK, keys 16 kb + v (from k0 + 4 G) above lim[qb]
   // are masked.  Returns whether any row's running max moved (then
   // alpha != 1 for it).
-  static constexpr int kPieceLag = 8;
+  static constexpr int kPieceLag = 4 * NKS - 40 > 8 ? 4 * NKS - 40 : 8;
   template <bool MASK>
   static __device__ __forceinline__ bool scores_softmax(const char* tile, const bf16x8 (*qf)[NKS], f32x4 (&s)[2][2],
                                                         const f32x4 (&sc)[2][2], const int (&lim)[2], float (&m_run)[2],
@@ -557,6 +559,11 @@ void flash_latent_bf16(const uint16_t* __restrict__ q_lat, const uint16_t* __res
     const uint64_t grew = __builtin_amdgcn_ballot_w64(grow);
     if (lane == 0) fbuf[w] = grew != 0;
     lds_publish_barrier();  // P and rescale factors of tile j posted
+    bf16x8 pq[F::NQ];
+#pragma unroll
+    for (int q = 0; q < F::NQ; ++q) pq[q] = lds_read16(pbuf + (q * 64 + lane) * 16);
+    const char* tile = smem + (j % kFlashBufs) * TILE;
+    bf16x8 a_next = cols(tile, cw);
     {
       const u32x4 f = *(const __attribute__((address_space(3))) u32x4*)(uintptr_t)fbuf;
       if ((f[0] | f[1] | f[2] | f[3]) != 0) {  // some row of the block has a new max
@@ -575,11 +582,6 @@ void flash_latent_bf16(const uint16_t* __restrict__ q_lat, const uint16_t* __res
       }
     }
     {
-      bf16x8 pq[F::NQ];
-#pragma unroll
-      for (int q = 0; q < F::NQ; ++q) pq[q] = lds_read16(pbuf + (q * 64 + lane) * 16);
-      const char* tile = smem + (j % kFlashBufs) * TILE;
-      bf16x8 a_next = cols(tile, cw);
 #pragma unroll
       for (int c = 0; c < F::NCW; ++c) {
         const bf16x8 av = a_next;

@@ -29,6 +29,18 @@ __device__ __forceinline__ void dma16(const void* gbase, uint32_t voff, uint32_t
       : "v"(voff), "s"(gbase), "s"(lds_base)
       : "memory");
 }
+// The same copy with M0 declared clobbered instead of saved and restored
+// (the compiler then keeps nothing in M0 across it): two scalar
+// instructions fewer per copy on the tile loops' issue path.
+__device__ __forceinline__ void dma16_m0(const void* gbase, uint32_t voff, uint32_t lds_base) {
+  asm volatile(
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %0, %1"
+      :
+      : "v"(voff), "s"(gbase), "s"(lds_base)
+      : "memory", "m0");
+}
 // Wait until at most n of this wave's vector-memory operations are outstanding.
 template <int n>
 __device__ __forceinline__ void dma_wait() {
@@ -78,6 +90,17 @@ __device__ __forceinline__ void dma_tile32(const uint16_t* latb, int k0, int ken
   if (REMAT) asm volatile("" : "+v"(lane));
   // with one row per instruction (R = 512) the row is wave-uniform
   const int sl = RPI == 1 ? 0 : (int)(lane / NC), p = (int)(lane % NC);
+  if (k0 + kTileKeys <= kend) {
+    // the whole tile is in range: no clamp; the same lane offsets as below
+    const uint16_t* tb = latb + (size_t)(k0 + w * RPI) * R;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int s = (4 * i + w) * RPI + sl;
+      const int c = (p & ~15) | ((p & 15) ^ tswz(s));
+      dma16_m0(tb + (size_t)4 * i * RPI * R, (uint32_t)(sl * R * 2 + 16 * c), tile + (4 * i + w) * 1024);
+    }
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < NI; ++i) {
     const int ins = 4 * i + w;       // wave-uniform
