@@ -77,6 +77,12 @@ struct Mha {
   static_assert(NSO == NPV, "one score op and one P*V op per slot");
 };
 
+// Keeps the computation of v at this point of the instruction stream: the
+// compiler otherwise sinks softmax values that are only read after the
+// rescale branch into the block behind it, out of the matrix-op slots.
+template <class T>
+__device__ __forceinline__ void pin(T& v) { asm volatile("" : "+v"(v)); }
+
 template <int D>
 constexpr size_t mha_lds_bytes() { return (size_t)kMhaBufs * Mha<D>::TILE; }
 
@@ -240,12 +246,15 @@ void flash_mha_bf16(const uint16_t* __restrict__ q, const uint16_t* __restrict__
       } else if (kp < 64) {  // probability u of row block qb, summed in pairs
         const int qb = kp & 3, u = (kp - 32) >> 2;
         x[qb][u] = fast_exp2(x[qb][u] - msub[qb]);
+        pin(x[qb][u]);
         if (u & 1) ps[qb] += x[qb][u - 1] + x[qb][u];
       } else if (kp < 80) {  // bf16 pairs, then the running sum and the P operand
         const int qb = kp & 3, u = (kp - 64) >> 2;
         pk[qb][u] = pack_bf16x2(x[qb][2 * u], x[qb][2 * u + 1]);
+        pin(pk[qb][u]);
         if (u == 3) {
           l_run[qb] = l_run[qb] * alpha[qb] + ps[qb];
+          pin(l_run[qb]);
           P[qb] = __builtin_bit_cast(bf16x8, u32x4{pk[qb][0], pk[qb][1], pk[qb][2], pk[qb][3]});
         }
       }
