@@ -56,13 +56,29 @@ __device__ __forceinline__ void static_for(F&& f) {
 //   scores: S^T[16 kb + 4 G + v][16 qb + n] in s[kb][qb][v] (A = K rows, B = q^T)
 //   P:      per qb the 8 probabilities of keys {16 kb + 4 G + v}: the P^T operand
 //   output: O^T[16 c + 4 G + v][16 qb + n] in o[c][qb][v]   (A = V^T by TileCols)
-// Per tile j the 32 score ops of tile j+1 alternate with the 32 P*V ops of
-// tile j-1 (whose P is ready), and the online softmax of tile j runs as 80
+// The row sums come from the matrix unit too: a ninth output block o[NCB]
+// multiplies P^T by an all-ones A operand, so every element of o[NCB][qb]
+// holds the sum of row 16 qb + n's bf16 probabilities, rescaled with O.
+// Per tile j the 32 score ops of tile j+1 alternate with the P*V ops of tile
+// j-1 (whose P is ready), and the online softmax of tile j runs as NPIECE
 // pieces between them; after them O is rescaled for tile j's maxima.  k
 // carries scale * log2 e, so scores are in log2 units.
-constexpr int kMhaBufs = 6;
-constexpr int kMhaAhead = 4;
+//
+// A single wave per SIMD issues one instruction at a time, so the loop is
+// written for instruction count: the ring has a power-of-two size, whole
+// tiles are copied with loop-invariant lane offsets, the four row maxima of
+// a lane are reduced and broadcast across its four 16-lane rows together
+// (twelve cross-lane instructions for all four), the rescale factor is only computed in
+// the (rare) rescale branch, and the loop runs two tiles per trip with the
+// score and probability registers swapping roles instead of being copied.
+constexpr int kMhaBufs = 8;
+constexpr int kMhaAhead = 6;
 constexpr int kMhaRows = 256;
+static_assert((kMhaBufs & (kMhaBufs - 1)) == 0, "ring slots by masking");
+// tile j + kMhaAhead reuses the slot of tile j + kMhaAhead - kMhaBufs, whose
+// last reader (P*V in iteration j + kMhaAhead - kMhaBufs + 1) finished before
+// the barrier that ends iteration j - 1
+static_assert(kMhaAhead <= kMhaBufs - 2 && kMhaAhead >= 3, "ring reuse distance");
 
 template <int D>
 struct Mha {
@@ -70,12 +86,15 @@ struct Mha {
   static constexpr int NCB = D / 16;          // 16-column blocks of the output
   static constexpr int NQB = 4;               // 16-row blocks of a wave
   static constexpr int NSO = 2 * NKS * NQB;   // score ops per tile
-  static constexpr int NPV = NCB * NQB;       // P*V ops per tile
+  static constexpr int NPV = NCB * NQB;       // P*V ops per tile (plus NQB row-sum ops)
   static constexpr int KT = 32 * D * 2;       // bytes of one K (or V) tile
   static constexpr int TILE = 2 * KT;
   static constexpr int NPIECE = 80;
   static_assert(NSO == NPV, "one score op and one P*V op per slot");
 };
+
+template <int D>
+constexpr size_t mha_lds_bytes() { return (size_t)kMhaBufs * Mha<D>::TILE; }
 
 // Keeps the computation of v at this point of the instruction stream: the
 // compiler otherwise sinks softmax values that are only read after the
@@ -83,8 +102,19 @@ struct Mha {
 template <class T>
 __device__ __forceinline__ void pin(T& v) { asm volatile("" : "+v"(v)); }
 
-template <int D>
-constexpr size_t mha_lds_bytes() { return (size_t)kMhaBufs * Mha<D>::TILE; }
+// permlane16_swap(a, b): the odd 16-lane rows of a trade places with the even
+// rows of b; returns the new (a, b).
+__device__ __forceinline__ void swap16(float& a, float& b) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+  a = __uint_as_float(r[0]);
+  b = __uint_as_float(r[1]);
+}
+// permlane32_swap(a, b): the upper 32 lanes of a trade places with the lower 32 of b.
+__device__ __forceinline__ void swap32(float& a, float& b) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+  a = __uint_as_float(r[0]);
+  b = __uint_as_float(r[1]);
+}
 
 template <int D>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
@@ -92,7 +122,9 @@ void flash_mha_bf16(const uint16_t* __restrict__ q, const uint16_t* __restrict__
                     const uint16_t* __restrict__ v, uint16_t* __restrict__ out, int B, int T, int H) {
   using M = Mha<D>;
   constexpr int NKS = M::NKS, NCB = M::NCB, NQB = M::NQB, KT = M::KT, TILE = M::TILE;
-  constexpr int NI = 2 * (KT / 1024 / 4);  // copy instructions per wave and tile (K and V)
+  constexpr int NIK = KT / 1024 / 4;  // copy instructions per wave for one K (or V) tile
+  constexpr int NI = 2 * NIK;         // ... for K and V
+  static_assert(NIK == 2 && D / 8 == 16, "whole-tile copies: two instructions of four rows per wave");
   extern __shared__ __attribute__((aligned(16))) char smem[];
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -110,31 +142,32 @@ void flash_mha_bf16(const uint16_t* __restrict__ q, const uint16_t* __restrict__
   const uint16_t* kbase = k + ((size_t)b * T * H + h) * D;
   const uint16_t* vbase = v + ((size_t)b * T * H + h) * D;
   const uint32_t lds0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)smem);
-  auto copy_tile = [&](int j) {
-    const uint32_t dst = lds0 + (j % kMhaBufs) * TILE;
-    dma_rows32<D>(kbase, stride, kTileKeys * j, T, dst, w);
-    dma_rows32<D>(vbase, stride, kTileKeys * j, T, dst + KT, w);
-  };
-  // wait until the own part of tile `need` landed (tiles are issued in order, each NI copies)
-  auto wait_tile = [&](int need, int issued) {
-    const int later = issued - 1 - need;  // tiles issued after it
-    if (later >= 3)
-      dma_wait<3 * NI>();
-    else if (later == 2)
-      dma_wait<2 * NI>();
-    else if (later == 1)
-      dma_wait<NI>();
-    else
-      dma_wait<0>();
+
+  // Whole-tile copies: copy instruction i of wave w moves key rows 16 i + 4 w
+  // .. + 3 (lane: row sl = lane / 16, chunk p = lane % 16, fetched for LDS
+  // chunk slot p, i.e. from chunk p ^ tswz(row)); tswz has period 16 in the
+  // row, so both instructions share the lane offset, the second 16 rows on.
+  const uint32_t voff0 = (uint32_t)((lane >> 4) * stride * 2 + 16 * ((lane & 15) ^ tswz(4 * w + (lane >> 4))));
+  const uint32_t voff1 = voff0 + (uint32_t)(16 * stride * 2);
+  const uint16_t* kw = kbase + 4 * w * stride;
+  const uint16_t* vw = vbase + 4 * w * stride;
+  auto copy_tile = [&](int t) {
+    const uint32_t dst = lds0 + (uint32_t)(t & (kMhaBufs - 1)) * TILE;
+    if (kTileKeys * t + kTileKeys <= T) {
+      const uint16_t* kt = kw + (size_t)kTileKeys * t * stride;
+      const uint16_t* vt = vw + (size_t)kTileKeys * t * stride;
+      dma16_m0(kt, voff0, dst + w * 1024);
+      dma16_m0(kt, voff1, dst + (4 + w) * 1024);
+      dma16_m0(vt, voff0, dst + KT + w * 1024);
+      dma16_m0(vt, voff1, dst + KT + (4 + w) * 1024);
+    } else {  // the ragged last tile: rows clamped to T - 1
+      dma_rows32<D>(kbase, stride, kTileKeys * t, T, dst, w);
+      dma_rows32<D>(vbase, stride, kTileKeys * t, T, dst + KT, w);
+    }
   };
 
-  int issued = 0;
-#pragma unroll
-  for (int t = 0; t < kMhaAhead; ++t)
-    if (t < ntiles) {
-      copy_tile(t);
-      ++issued;
-    }
+  const int npro = ntiles < kMhaAhead ? ntiles : kMhaAhead;
+  for (int t = 0; t < npro; ++t) copy_tile(t);
   // q rows of the lane: t = tw0 + 16 qb + n; B operand q^T[32 ks + 8 G ..][n]
   int t_row[NQB];
   bf16x8 qf[NQB][NKS];
@@ -154,138 +187,177 @@ void flash_mha_bf16(const uint16_t* __restrict__ q, const uint16_t* __restrict__
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) asm volatile("" : : "v"(qf[qb][ks]));
 
-  f32x4 o[NCB][NQB];
+  f32x4 o[NCB + 1][NQB];
 #pragma unroll
-  for (int c = 0; c < NCB; ++c)
+  for (int c = 0; c <= NCB; ++c)
 #pragma unroll
     for (int qb = 0; qb < NQB; ++qb) o[c][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run[NQB], l_run[NQB];
+  float m_run[NQB], m_thr[NQB];
 #pragma unroll
   for (int qb = 0; qb < NQB; ++qb) {
     m_run[qb] = -INFINITY;
-    l_run[qb] = 0.f;
+    m_thr[qb] = -INFINITY;
   }
-  const TileCols<D> cols;
-  const int f = tswz(n);  // score reads: key rows n and 16 + n
-  auto rd_k = [&](const char* kt, int r) {  // read r = 2 ks + kb: key row 16 kb + n, chunk 4 ks + G
-    const int kb = r & 1, ks = r >> 1;
-    const int c = 4 * ks + G;
-    return lds_read16(kt + (16 * kb + n) * (D * 2) + 16 * (c ^ f));
+  // The all-ones A operand of the row-sum ops, produced by an asm so that the
+  // compiler keeps it in registers instead of re-creating it next to a matrix
+  // op (a VALU write just before a matrix op reads it is a hazard the
+  // compiler does not see inside inline asm).
+  uint32_t one2;
+  asm volatile("v_mov_b32 %0, 0x3f803f80" : "=v"(one2));
+  const bf16x8 ones = __builtin_bit_cast(bf16x8, u32x4{one2, one2, one2, one2});
+
+  // LDS read offsets, loop-invariant: K rows 16 kb + n, chunk 4 ks + G
+  // (kb = 1 is 16 rows on, an immediate offset); V^T columns by TileCols.
+  uint32_t koff[NKS];
+  {
+    const int f = tswz(n);
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) koff[ks] = (uint32_t)(n * (D * 2) + 16 * ((4 * ks + G) ^ f));
+  }
+  uint32_t vcol[NCB];
+  {
+    const int key = 4 * G + (n >> 2), fk = tswz(key), sub = 8 * (n & 1), half = (n & 3) >> 1;
+#pragma unroll
+    for (int c = 0; c < NCB; ++c) {
+      const int ch = 2 * c + half;
+      vcol[c] = (uint32_t)(KT + key * (D * 2) + 16 * ((ch & ~15) | ((ch & 15) ^ fk)) + sub);
+    }
+  }
+  auto rd_k = [&](uint32_t slot, int r) {  // read r = 2 ks + kb
+    return lds_read16(smem + slot + koff[r >> 1] + (r & 1) * 16 * (D * 2));
+  };
+  auto rd_v = [&](uint32_t slot, int c) {  // A operand V^T rows 16 c .., keys 4 G + u and 16 + 4 G + u
+    const char* p = smem + slot + vcol[c];
+    const i16x4 a0 = lds_read_tr16(p);
+    const i16x4 a1 = lds_read_tr16(p + 16 * (D * 2));
+    return __builtin_bit_cast(bf16x8, u32x4{__builtin_bit_cast(u32x2, a0)[0], __builtin_bit_cast(u32x2, a0)[1],
+                                            __builtin_bit_cast(u32x2, a1)[0], __builtin_bit_cast(u32x2, a1)[1]});
   };
 
-  // scores of tile 0
-  wait_tile(ntiles > 1 ? 1 : 0, issued);
+  // tiles 0 and 1 landed (own part), then everyone's
+  if (ntiles >= kMhaAhead)
+    dma_wait<(kMhaAhead - 2) * NI>();
+  else
+    dma_wait<0>();
   __builtin_amdgcn_s_barrier();
-  f32x4 s_cur[2][NQB];
+  f32x4 sA[2][NQB], sB[2][NQB];
+  bf16x8 PA[NQB], PB[NQB];
   {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int qb = 0; qb < NQB; ++qb) s_cur[kb][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int qb = 0; qb < NQB; ++qb) sA[kb][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int r = 0; r < 2 * NKS; ++r) {
-      const bf16x8 a = rd_k(smem, r);
+      const bf16x8 a = rd_k(0, r);
 #pragma unroll
-      for (int qb = 0; qb < NQB; ++qb) s_cur[r & 1][qb] = mfma16x16x32(a, qf[qb][r >> 1], s_cur[r & 1][qb]);
+      for (int qb = 0; qb < NQB; ++qb) sA[r & 1][qb] = mfma16x16x32(a, qf[qb][r >> 1], sA[r & 1][qb]);
     }
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb) PA[qb] = bf16x8{};
   }
-  bf16x8 P_prev[NQB];
-#pragma unroll
-  for (int qb = 0; qb < NQB; ++qb) P_prev[qb] = bf16x8{};
 
-  // Iteration j; with MASK, keys above a row's position are masked (only
-  // tiles that reach past the wave's first row need it).
-  auto body = [&](int j, auto maskc) __attribute__((always_inline)) {
-    constexpr bool mask = decltype(maskc)::value;
-    const int k0 = kTileKeys * j;
-    const char* ktile = smem + ((j + 1) % kMhaBufs) * TILE;                   // scores of tile j + 1
-    const char* vtile = smem + ((j > 0 ? j - 1 : 0) % kMhaBufs) * TILE + KT;  // P*V of tile j - 1
-    int lim[NQB];
+  // tiles below every row of the wave need no mask
+  const int jm = tw0 / kTileKeys < ntiles ? tw0 / kTileKeys : ntiles;
+  // Iteration j: softmax of tile j (scores in sc, probabilities out in Pn),
+  // scores of tile j + 1 into sn, P*V of tile j - 1 from Pp.  Tiles that
+  // reach past the wave's first row first get keys above a row's position
+  // masked, in a branch of their own ahead of the slots.
+  auto body = [&](int j, f32x4 (&sc)[2][NQB], f32x4 (&sn)[2][NQB], bf16x8 (&Pp)[NQB],
+                  bf16x8 (&Pn)[NQB]) __attribute__((always_inline)) {
+    const uint32_t kslot = (uint32_t)((j + 1) & (kMhaBufs - 1)) * TILE;                 // scores of tile j + 1
+    const uint32_t vslot = (uint32_t)((j > 0 ? j - 1 : 0) & (kMhaBufs - 1)) * TILE;     // P*V of tile j - 1
+    if (j >= jm) {
 #pragma unroll
-    for (int qb = 0; qb < NQB; ++qb) lim[qb] = t_row[qb] - k0 - 4 * G;
+      for (int qb = 0; qb < NQB; ++qb) {
+        const int lim = t_row[qb] - kTileKeys * j - 4 * G;  // last visible key offset 16 kb + u
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (16 * (e >> 2) + (e & 3) > lim) sc[e >> 2][qb][e & 3] = -INFINITY;
+      }
+    }
 
-    // softmax state of this tile
-    float x[NQB][8], mm[NQB][4], mt[NQB], ps[NQB], msub[NQB], alpha[NQB];
+    float mt[NQB], msub[NQB];
     bool grow[NQB];
     uint32_t pk[NQB][4];
-    bf16x8 P[NQB];
+    // element e = 4 kb + u of row block qb: sc[kb][qb][u]
+    float x[NQB][8];
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[qb][e] = sc[e >> 2][qb][e & 3];
     auto piece = [&](int kp) __attribute__((always_inline)) {
-      if (kp < 16) {  // masking and the lane's maximum of row block kp / 4
+      if (kp < 16) {  // the lane's maximum of row block kp / 4
         const int qb = kp >> 2, part = kp & 3;
         if (part == 0) {
-#pragma unroll
-          for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int u = 0; u < 4; ++u)
-              x[qb][4 * kb + u] = (mask && 16 * kb + u > lim[qb]) ? -INFINITY : s_cur[kb][qb][u];
-          mm[qb][0] = fmaxf(x[qb][0], x[qb][1]);
-          mm[qb][1] = fmaxf(x[qb][2], x[qb][3]);
+          mt[qb] = fmaxf(fmaxf(x[qb][0], x[qb][1]), x[qb][2]);
         } else if (part == 1) {
-          mm[qb][2] = fmaxf(x[qb][4], x[qb][5]);
-          mm[qb][3] = fmaxf(x[qb][6], x[qb][7]);
+          mt[qb] = fmaxf(fmaxf(mt[qb], x[qb][3]), x[qb][4]);
         } else if (part == 2) {
-          mm[qb][0] = fmaxf(mm[qb][0], mm[qb][1]);
-          mm[qb][2] = fmaxf(mm[qb][2], mm[qb][3]);
+          mt[qb] = fmaxf(fmaxf(mt[qb], x[qb][5]), x[qb][6]);
         } else {
-          mt[qb] = fmaxf(mm[qb][0], mm[qb][2]);
+          mt[qb] = fmaxf(mt[qb], x[qb][7]);
         }
-      } else if (kp < 24) {  // maximum over the four lanes of a row
+      } else if (kp < 28) {
+        // Row maxima over the four 16-lane rows, all four row blocks at once:
+        // after the pair swaps and the 32-lane swap, row g of mt[0] holds the
+        // maximum of row block g; three more swaps broadcast it to every row.
+        switch (kp) {
+          case 16: swap16(mt[0], mt[1]); break;
+          case 17: mt[0] = fmaxf(mt[0], mt[1]); break;
+          case 18: swap16(mt[2], mt[3]); break;
+          case 19: mt[2] = fmaxf(mt[2], mt[3]); break;
+          case 20: swap32(mt[0], mt[2]); break;
+          case 21: mt[0] = fmaxf(mt[0], mt[2]); break;
+          case 22: mt[2] = mt[0]; break;
+          case 23: swap32(mt[0], mt[2]); break;  // mt[0]: rows (0, 1, 0, 1); mt[2]: (2, 3, 2, 3)
+          case 24: mt[1] = mt[0]; break;
+          case 25: swap16(mt[0], mt[1]); break;  // block 0 everywhere in mt[0], block 1 in mt[1]
+          case 26: mt[3] = mt[2]; break;
+          default: swap16(mt[2], mt[3]); break;  // blocks 2 and 3
+        }
+      } else if (kp < 32) {  // lazy rescale: a new reference only if the max moved past the slack
         const int qb = kp & 3;
-        mt[qb] = kp < 20 ? max_xor16(mt[qb]) : max_xor32(mt[qb]);
-      } else if (kp < 28) {  // rescale factor
-        const int qb = kp & 3;
-        grow[qb] = mt[qb] > m_run[qb] + kRescaleSlack;
-        alpha[qb] = grow[qb] ? fast_exp2(m_run[qb] - mt[qb]) : 1.f;
-      } else if (kp < 32) {  // running max
-        const int qb = kp & 3;
-        m_run[qb] = grow[qb] ? mt[qb] : m_run[qb];
-        // finite from tile 0 on: key 0 is unmasked for every row, so the
-        // first tile always moves the running max off -infinity
-        msub[qb] = m_run[qb];
-        ps[qb] = 0.f;
-      } else if (kp < 64) {  // probability u of row block qb, summed in pairs
-        const int qb = kp & 3, u = (kp - 32) >> 2;
-        x[qb][u] = fast_exp2(x[qb][u] - msub[qb]);
-        pin(x[qb][u]);
-        if (u & 1) ps[qb] += x[qb][u - 1] + x[qb][u];
-      } else if (kp < 80) {  // bf16 pairs, then the running sum and the P operand
+        grow[qb] = mt[qb] > m_thr[qb];
+        msub[qb] = grow[qb] ? mt[qb] : m_run[qb];
+      } else if (kp < 64) {  // probability e of row block qb
+        const int qb = kp & 3, e = (kp - 32) >> 2;
+        x[qb][e] = fast_exp2(x[qb][e] - msub[qb]);
+        pin(x[qb][e]);
+      } else if (kp < 80) {  // bf16 pairs, then the P operand
         const int qb = kp & 3, u = (kp - 64) >> 2;
         pk[qb][u] = pack_bf16x2(x[qb][2 * u], x[qb][2 * u + 1]);
         pin(pk[qb][u]);
-        if (u == 3) {
-          l_run[qb] = l_run[qb] * alpha[qb] + ps[qb];
-          pin(l_run[qb]);
-          P[qb] = __builtin_bit_cast(bf16x8, u32x4{pk[qb][0], pk[qb][1], pk[qb][2], pk[qb][3]});
-        }
+        if (u == 3) Pn[qb] = __builtin_bit_cast(bf16x8, u32x4{pk[qb][0], pk[qb][1], pk[qb][2], pk[qb][3]});
       }
     };
 
-    // slot i: score op i of tile j + 1, then P*V op i of tile j - 1; pieces between
-    f32x4 s_next[2][NQB];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int qb = 0; qb < NQB; ++qb) s_next[kb][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // slot i: score op i of tile j + 1, then P*V op i of tile j - 1 (and, in
+    // the last slot of each column step pair, a row-sum op); pieces between
     constexpr int NSLOT = M::NSO, NR = 2 * NKS;
     bf16x8 kr[3], vr[3];
-    kr[0] = rd_k(ktile, 0);
-    kr[1] = rd_k(ktile, 1);
-    vr[0] = cols(vtile, 0);
-    vr[1] = cols(vtile, 16);
+    kr[0] = rd_k(kslot, 0);
+    kr[1] = rd_k(kslot, 1);
+    vr[0] = rd_v(vslot, 0);
+    vr[1] = rd_v(vslot, 1);
     static_for<NSLOT>([&](auto ic) __attribute__((always_inline)) {
       constexpr int i = decltype(ic)::value;
       {
         constexpr int r = i / NQB, qb = i % NQB;
-        if constexpr (qb == 0 && r + 2 < NR) kr[(r + 2) % 3] = rd_k(ktile, r + 2);
-        s_next[r & 1][qb] = mfma16x16x32(kr[r % 3], qf[qb][r >> 1], s_next[r & 1][qb]);
+        if constexpr (qb == 0 && r + 2 < NR) kr[(r + 2) % 3] = rd_k(kslot, r + 2);
+        if constexpr (r < 2)
+          sn[r & 1][qb] = mfma16x16x32(kr[r % 3], qf[qb][r >> 1], f32x4{0.f, 0.f, 0.f, 0.f});
+        else
+          sn[r & 1][qb] = mfma16x16x32(kr[r % 3], qf[qb][r >> 1], sn[r & 1][qb]);
       }
 #pragma unroll
       for (int kp = (2 * i) * M::NPIECE / (2 * NSLOT); kp < (2 * i + 1) * M::NPIECE / (2 * NSLOT); ++kp) piece(kp);
       __builtin_amdgcn_sched_barrier(0);
       {
         constexpr int c = i / NQB, qb = i % NQB;
-        if constexpr (qb == 0 && c + 2 < NCB) vr[(c + 2) % 3] = cols(vtile, 16 * (c + 2));
-        mfma16x16x32_a(o[c][qb], vr[c % 3], P_prev[qb]);
+        if constexpr (qb == 0 && c + 2 < NCB) vr[(c + 2) % 3] = rd_v(vslot, c + 2);
+        mfma16x16x32_a(o[c][qb], vr[c % 3], Pp[qb]);
+        if constexpr (i % 8 == 7) mfma16x16x32_a(o[NCB][i / 8], ones, Pp[i / 8]);
       }
 #pragma unroll
       for (int kp = (2 * i + 1) * M::NPIECE / (2 * NSLOT); kp < (2 * i + 2) * M::NPIECE / (2 * NSLOT); ++kp)
@@ -293,14 +365,21 @@ void flash_mha_bf16(const uint16_t* __restrict__ q, const uint16_t* __restrict__
       __builtin_amdgcn_sched_barrier(0);
     });
 
-    // O holds tile j - 1 now: move it to tile j's maxima
+    // O and the row sums hold tile j - 1 now: move them to tile j's maxima
     bool any = false;
 #pragma unroll
     for (int qb = 0; qb < NQB; ++qb) any |= grow[qb];
     if (__builtin_amdgcn_ballot_w64(any)) {
+      float alpha[NQB];
+#pragma unroll
+      for (int qb = 0; qb < NQB; ++qb) {
+        alpha[qb] = fast_exp2(m_run[qb] - msub[qb]);  // 1 where the reference stayed
+        m_run[qb] = msub[qb];
+        m_thr[qb] = msub[qb] + kRescaleSlack;
+      }
       mfma_agpr_wait();
 #pragma unroll
-      for (int c = 0; c < NCB; ++c)
+      for (int c = 0; c <= NCB; ++c)
 #pragma unroll
         for (int qb = 0; qb < NQB; ++qb) {
           mfma_agpr_tie(o[c][qb]);
@@ -308,54 +387,50 @@ void flash_mha_bf16(const uint16_t* __restrict__ q, const uint16_t* __restrict__
           mfma_agpr_tie(o[c][qb]);
         }
     }
-#pragma unroll
-    for (int qb = 0; qb < NQB; ++qb) P_prev[qb] = P[qb];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int qb = 0; qb < NQB; ++qb) s_cur[kb][qb] = s_next[kb][qb];
-    // refill the buffer of tile j - 2 (its last reader, P*V of j - 2, ended last iteration)
+    // refill the slot of tile j + kMhaAhead - kMhaBufs; tile j + 2 (own part) landed before the barrier
     if (j + kMhaAhead < ntiles) {
       copy_tile(j + kMhaAhead);
-      ++issued;
+      dma_wait<(kMhaAhead - 2) * NI>();
+    } else {
+      dma_wait<0>();
     }
-    // own part of tile j + 2 landed before the barrier that ends the iteration
-    if (j + 2 < ntiles) wait_tile(j + 2, issued);
     __builtin_amdgcn_s_barrier();
   };
-  const int jm = tw0 / kTileKeys < ntiles ? tw0 / kTileKeys : ntiles;  // tiles below every row of the wave
-  for (int j = 0; j < jm; ++j) body(j, std::false_type{});
-  for (int j = jm; j < ntiles; ++j) body(j, std::true_type{});
+  // Two tiles per trip, the registers swapping roles.  An odd count runs one
+  // phantom tile j = ntiles at the end: every key of it lies above every row
+  // of the block, so the mask branch turns its (stale) scores into -inf and
+  // its probabilities into 0, and its iteration does the P*V of the real
+  // last tile; the epilogue then has no P*V left to do.
+  for (int j = 0; j < ntiles; j += 2) {
+    body(j, sA, sB, PA, PB);
+    body(j + 1, sB, sA, PB, PA);
+  }
 
-  // P*V of the last tile
-  {
-    const char* vtile = smem + ((ntiles - 1) % kMhaBufs) * TILE + KT;
+  // P*V and row sums of the last tile (even counts)
+  if (!(ntiles & 1)) {
+    const uint32_t vslot = (uint32_t)((ntiles - 1) & (kMhaBufs - 1)) * TILE;
 #pragma unroll
     for (int c = 0; c < NCB; ++c) {
-      const bf16x8 a = cols(vtile, 16 * c);
+      const bf16x8 a = rd_v(vslot, c);
 #pragma unroll
-      for (int qb = 0; qb < NQB; ++qb) mfma16x16x32_a(o[c][qb], a, P_prev[qb]);
+      for (int qb = 0; qb < NQB; ++qb) mfma16x16x32_a(o[c][qb], a, PA[qb]);
     }
-  }
-  // l of each row from its four lanes, then the normalised rows
-  float inv[NQB];
 #pragma unroll
-  for (int qb = 0; qb < NQB; ++qb) {
-    float l = l_run[qb] + __shfl_xor(l_run[qb], 16);
-    l += __shfl_xor(l, 32);
-    inv[qb] = 1.f / l;
+    for (int qb = 0; qb < NQB; ++qb) mfma16x16x32_a(o[NCB][qb], ones, PA[qb]);
   }
   mfma_agpr_wait();
 #pragma unroll
   for (int qb = 0; qb < NQB; ++qb) {
     const int t = tw0 + 16 * qb + n;
+    mfma_agpr_tie(o[NCB][qb]);
+    const float inv = 1.f / o[NCB][qb][0];
     if (t >= T) continue;
     uint16_t* orow = out + (((size_t)b * T + t) * H + h) * D + 4 * G;
 #pragma unroll
     for (int c = 0; c < NCB; ++c) {
       mfma_agpr_tie(o[c][qb]);
-      const u32x2 val = {pack_bf16x2(o[c][qb][0] * inv[qb], o[c][qb][1] * inv[qb]),
-                         pack_bf16x2(o[c][qb][2] * inv[qb], o[c][qb][3] * inv[qb])};
+      const u32x2 val = {pack_bf16x2(o[c][qb][0] * inv, o[c][qb][1] * inv),
+                         pack_bf16x2(o[c][qb][2] * inv, o[c][qb][3] * inv)};
       *(u32x2*)(orow + 16 * c) = val;
     }
   }

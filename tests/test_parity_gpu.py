@@ -232,12 +232,13 @@ def test_prefill_beyond_int32_offsets_sampled():
 
 # ---------------------------------------------------------------- unabsorbed prefill (k, v materialised)
 UNABSORBED_SMALL = [
-    dict(B=2, T=300, H=3),            # two 256-row blocks, ragged tail, ring of six tiles wrapped
-    dict(B=1, T=520, H=1),            # 17 tiles: the ring wraps twice; partial last row block
-    dict(B=3, T=1, H=2),              # single key
+    dict(B=2, T=300, H=3),            # two 256-row blocks, ragged tail, ring of eight tiles wrapped
+    dict(B=1, T=520, H=1),            # 17 tiles (odd: a phantom tile ends the loop); partial last row block
+    dict(B=3, T=1, H=2),              # single key, one tile
     dict(B=1, T=33, H=4, r=256),      # r = 256
-    dict(B=2, T=65, H=2, r=128),      # r = 128
+    dict(B=2, T=65, H=2, r=128),      # r = 128, three tiles, the last one key
     dict(B=1, T=64, H=2),             # a whole number of tiles, fewer than the copy distance
+    dict(B=1, T=800, H=2),            # blocks of 8, 16, 24 and 25 whole tiles: odd count, no ragged tile
 ]
 
 
