@@ -119,7 +119,7 @@ __device__ __forceinline__ void swap32(float& a, float& b) {
 template <int D>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
 void flash_mha_bf16(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
-                    const uint16_t* __restrict__ v, uint16_t* __restrict__ out, int B, int T, int H) {
+                    const uint16_t* __restrict__ v, uint16_t* __restrict__ out, int B, int T, int H, int grp) {
   using M = Mha<D>;
   constexpr int NKS = M::NKS, NCB = M::NCB, NQB = M::NQB, KT = M::KT, TILE = M::TILE;
   constexpr int NIK = KT / 1024 / 4;  // copy instructions per wave for one K (or V) tile
@@ -131,8 +131,24 @@ void flash_mha_bf16(const uint16_t* __restrict__ q, const uint16_t* __restrict__
   const int G = lane >> 4, n = lane & 15;
   const int nqb = (T + kMhaRows - 1) / kMhaRows;
   const int BH = B * H;
-  const int qblk = nqb - 1 - (int)(blockIdx.x / BH);  // heaviest first
-  const int bh = (int)(blockIdx.x % BH);
+  // Block i runs on XCD i % 8 (round-robin dispatch).  With grp > 0 (B * H
+  // a multiple of 8, nqb a multiple of grp) XCD x takes the heads bh = x
+  // (mod 8) and walks grp row blocks of one head, heaviest first, then the
+  // same levels of its next head, and so on, before the next grp levels: the
+  // blocks an XCD runs at a time then stream fewer heads' K and V, close
+  // together, through its L2, while the order stays heaviest first in steps
+  // of grp levels.  Otherwise all heads' heaviest row blocks go first.
+  int qidx, bh;  // qidx 0 = the heaviest row block
+  if (grp > 0) {
+    const int m = (int)(blockIdx.x >> 3), hx = BH >> 3;
+    const int lvl = m / (grp * hx), r = m % (grp * hx);
+    qidx = grp * lvl + r % grp;
+    bh = 8 * (r / grp) + (int)(blockIdx.x & 7);
+  } else {
+    qidx = (int)(blockIdx.x / BH);
+    bh = (int)(blockIdx.x % BH);
+  }
+  const int qblk = nqb - 1 - qidx;
   const int b = bh / H, h = bh % H;
   const int t0 = qblk * kMhaRows;
   const int t_last = t0 + kMhaRows - 1 < T - 1 ? t0 + kMhaRows - 1 : T - 1;
@@ -466,8 +482,15 @@ hipError_t prefill_unabsorbed(const void* q, const void* lat, const void* wk, co
   const int nqb = (T + kMhaRows - 1) / kMhaRows;
   {
     ProfScope ps("flash_mha_bf16", st);
+    // Whole heads per XCD when every compute unit runs many blocks (the
+    // heaviest block is then a small part of a unit's work, and a late start
+    // of it costs little): at bf16_long_prefill (32 blocks per unit) 9.27 ->
+    // 8.48 ms.  With few blocks per unit, heaviest first: at bf16_prefill (4
+    // per unit) whole heads took 0.187 -> 0.253 ms.
+    int grp = 0;
+    if ((B * H) % 8 == 0) grp = (long)B * H * nqb >= 16L * device_cus() ? nqb : 1;
     hipLaunchKernelGGL(flash_mha_bf16<128>, dim3(B * H * nqb), dim3(256), mha_lds_bytes<128>(), st,
-                       (const uint16_t*)q, kk, vv, (uint16_t*)out, B, T, H);
+                       (const uint16_t*)q, kk, vv, (uint16_t*)out, B, T, H, grp);
   }
   return hipGetLastError();
 }

@@ -239,6 +239,8 @@ UNABSORBED_SMALL = [
     dict(B=2, T=65, H=2, r=128),      # r = 128, three tiles, the last one key
     dict(B=1, T=64, H=2),             # a whole number of tiles, fewer than the copy distance
     dict(B=1, T=800, H=2),            # blocks of 8, 16, 24 and 25 whole tiles: odd count, no ragged tile
+    dict(B=2, T=530, H=4),            # B * H = 8: heads grouped by XCD; blocks of 8, 16 and 17 tiles
+    dict(B=1, T=96, H=16),            # B * H = 16, one row block per head
 ]
 
 
