@@ -96,26 +96,6 @@ struct Mha {
 template <int D>
 constexpr size_t mha_lds_bytes() { return (size_t)kMhaBufs * Mha<D>::TILE; }
 
-// Keeps the computation of v at this point of the instruction stream: the
-// compiler otherwise sinks softmax values that are only read after the
-// rescale branch into the block behind it, out of the matrix-op slots.
-template <class T>
-__device__ __forceinline__ void pin(T& v) { asm volatile("" : "+v"(v)); }
-
-// permlane16_swap(a, b): the odd 16-lane rows of a trade places with the even
-// rows of b; returns the new (a, b).
-__device__ __forceinline__ void swap16(float& a, float& b) {
-  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
-  a = __uint_as_float(r[0]);
-  b = __uint_as_float(r[1]);
-}
-// permlane32_swap(a, b): the upper 32 lanes of a trade places with the lower 32 of b.
-__device__ __forceinline__ void swap32(float& a, float& b) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
-  a = __uint_as_float(r[0]);
-  b = __uint_as_float(r[1]);
-}
-
 template <int D>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
 void flash_mha_bf16(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,

@@ -77,6 +77,26 @@ __device__ __forceinline__ float max_xor16(float v) {
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
+// Keeps the computation of v at this point of the instruction stream: the
+// compiler otherwise sinks softmax values that are only read after a
+// rescale branch into the block behind it, out of the matrix-op slots.
+template <class T>
+__device__ __forceinline__ void pin(T& v) { asm volatile("" : "+v"(v)); }
+
+// permlane16_swap(a, b): the odd 16-lane rows of a trade places with the even
+// rows of b.
+__device__ __forceinline__ void swap16(float& a, float& b) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+  a = __uint_as_float(r[0]);
+  b = __uint_as_float(r[1]);
+}
+// permlane32_swap(a, b): the upper 32 lanes of a trade places with the lower 32 of b.
+__device__ __forceinline__ void swap32(float& a, float& b) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+  a = __uint_as_float(r[0]);
+  b = __uint_as_float(r[1]);
+}
+
 // LDS transpose read: within each group of 16 lanes, element k of lane i is
 // element i%4 of the 8 bytes addressed by lane 4k + i/4.
 // 2^x by the hardware exponential alone (no range reduction for results
