@@ -97,8 +97,6 @@ __device__ __forceinline__ void swap32(float& a, float& b) {
   b = __uint_as_float(r[1]);
 }
 
-// LDS transpose read: within each group of 16 lanes, element k of lane i is
-// element i%4 of the 8 bytes addressed by lane 4k + i/4.
 // 2^x by the hardware exponential alone (no range reduction for results
 // below the smallest normal float, which flush to zero): softmax weights are
 // 2^(x - m) with x - m <= 8, where such results are negligible.
@@ -111,6 +109,8 @@ __device__ __forceinline__ bf16x8 lds_read16(const void* lds_byte_addr) {
   return *(const __attribute__((address_space(3))) bf16x8*)(uintptr_t)lds_byte_addr;
 }
 
+// LDS transpose read: within each group of 16 lanes, element k of lane i is
+// element i%4 of the 8 bytes addressed by lane 4k + i/4.
 __device__ __forceinline__ i16x4 lds_read_tr16(const void* lds_byte_addr) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)lds_byte_addr);
 }
