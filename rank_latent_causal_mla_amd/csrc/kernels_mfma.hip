@@ -194,15 +194,20 @@ hipError_t transpose_wv_launch(const uint16_t* wv, uint16_t* wvT, int R, int H, 
 // registers), and row blocks kUpRowBlocks * blockIdx.x .. of 32 rows.  The
 // o_lat rows of a row block are copied once per block into LDS by LDS-DMA
 // (two buffers, the next block's copy in flight), chunk-swizzled by the row
-// so the four waves' operand reads are conflict-free.
+// so the four waves' operand reads are conflict-free.  Blocks with blockIdx.z
+// >= zsplit compute a second product of the same rows (W2, out2, oscale2):
+// k and v from the latent in one launch.
 constexpr int kUpRowBlocks = 32;
 template <int R>
 constexpr size_t up_lds_bytes() { return (size_t)2 * 32 * R * 2; }
 
 template <int R, bool SHARED>
 __global__ __launch_bounds__(256, 2) void up_bf16(const uint16_t* __restrict__ o_lat,
-                                                  const uint16_t* __restrict__ wvT,
-                                                  uint16_t* __restrict__ out, int N, int H, int d, float oscale) {
+                                                  const uint16_t* __restrict__ wvT1,
+                                                  uint16_t* __restrict__ out1, float oscale1,
+                                                  const uint16_t* __restrict__ wvT2,
+                                                  uint16_t* __restrict__ out2, float oscale2, int zsplit,
+                                                  int N, int H, int d) {
   constexpr int NKS = R / 16;           // contraction steps
   constexpr int TB = 32 * R * 2;        // one row block in LDS
   constexpr int NC = R / 8;             // 16-byte chunks per row
@@ -214,7 +219,11 @@ __global__ __launch_bounds__(256, 2) void up_bf16(const uint16_t* __restrict__ o
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane >> 5, l32 = lane & 31;
   const int h = blockIdx.y;
-  const int i = 4 * blockIdx.z + w;  // output block of 32 columns
+  const bool second = (int)blockIdx.z >= zsplit;
+  const uint16_t* __restrict__ wvT = second ? wvT2 : wvT1;
+  uint16_t* __restrict__ out = second ? out2 : out1;
+  const float oscale = second ? oscale2 : oscale1;
+  const int i = 4 * ((int)blockIdx.z - (second ? zsplit : 0)) + w;  // output block of 32 columns
   const bool has_cols = i < d / 32;
   const int nb0 = blockIdx.x * kUpRowBlocks;
   const int nrb_all = (N + 31) / 32;
@@ -854,8 +863,9 @@ static hipError_t run_prefill(const uint16_t* q, const uint16_t* lat, const uint
   }
   {
     ProfScope ps("up_bf16", st);
-    hipLaunchKernelGGL((up_bf16<R, false>), dim3((N + 32 * kUpRowBlocks - 1) / (32 * kUpRowBlocks), H, (d + 127) / 128),
-                       dim3(256), up_lds_bytes<R>(), st, o_lat, wvT, out, N, H, d, 1.0f);
+    const int zb = (d + 127) / 128;
+    hipLaunchKernelGGL((up_bf16<R, false>), dim3((N + 32 * kUpRowBlocks - 1) / (32 * kUpRowBlocks), H, zb),
+                       dim3(256), up_lds_bytes<R>(), st, o_lat, wvT, out, 1.0f, wvT, out, 1.0f, zb, N, H, d);
   }
   return hipGetLastError();
 }
@@ -903,11 +913,12 @@ static hipError_t run_materialise(const uint16_t* lat, const uint16_t* wk, const
     if (e == hipSuccess) e = transpose_wv_launch(wv, wvT, R, H, d, st);
     if (e != hipSuccess) return e;
   }
-  const dim3 grid((N + 32 * kUpRowBlocks - 1) / (32 * kUpRowBlocks), H, (d + 127) / 128);
+  const int zb = (d + 127) / 128;  // column blocks of one product; k then v along z
+  const dim3 grid((N + 32 * kUpRowBlocks - 1) / (32 * kUpRowBlocks), H, 2 * zb);
   {
     ProfScope ps("materialise_kv", st);
-    hipLaunchKernelGGL((up_bf16<R, true>), grid, dim3(256), up_lds_bytes<R>(), st, lat, wkT, k, N, H, d, kscale);
-    hipLaunchKernelGGL((up_bf16<R, true>), grid, dim3(256), up_lds_bytes<R>(), st, lat, wvT, v, N, H, d, 1.0f);
+    hipLaunchKernelGGL((up_bf16<R, true>), grid, dim3(256), up_lds_bytes<R>(), st, lat, wkT, k, kscale, wvT, v, 1.0f,
+                       zb, N, H, d);
   }
   return hipGetLastError();
 }
