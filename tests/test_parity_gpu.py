@@ -9,7 +9,7 @@ import pytest
 import oracle
 import rank_latent_causal_mla_amd as mla
 import synth
-from tests.helpers import compare, to_device, to_f64
+from tests.helpers import TOL, compare, to_device, to_f64
 
 pytestmark = pytest.mark.gpu
 
@@ -259,6 +259,39 @@ def test_unabsorbed_prefill_matches_oracle(kw):
 def test_unabsorbed_bf16_prefill_full_size_sampled():
     sampled_prefill(synth.CONFIGS["bf16_prefill"], heads=[(0, 0), (3, 7), (7, 15)], rows_per_head=24,
                     fwd=mla.mla_latent_attn_fwd_unabsorbed)
+
+
+def test_unabsorbed_bf16_long_prefill_every_head_sampled():
+    """The unabsorbed form at bf16_long_prefill's full size (32 row blocks per
+    compute unit: the kernel walks whole heads per XCD) on the rows of the
+    absorbed every-head test: every (b, h) pair near the first tiles and row
+    blocks, 16 pairs at the middle and last rows."""
+    cfg = synth.CONFIGS["bf16_long_prefill"]
+    T = cfg.T
+    early = (0, 1, 31, 32, 33, 127, 128, 255, 256)
+    entries = [(b, h, t) for b in range(cfg.B) for h in range(cfg.H) for t in early]
+    entries += [(b, h, t) for b in range(cfg.B) for h in range(b + 3, cfg.H, 8) for t in (T // 2, T - 1)]
+    sampled_rows(cfg, entries, fwd=mla.mla_latent_attn_fwd_unabsorbed, what="every head, unabsorbed")
+
+
+@pytest.mark.parametrize("name", ["bf16_prefill", "bf16_long_prefill"])
+def test_unabsorbed_agrees_with_absorbed_everywhere(name):
+    """Every output element of the two forms at full size, on the GPU: both
+    are within the bf16 bar of the oracle, so they agree within twice it.  A
+    row block that one form skipped or wrote twice would not."""
+    import torch
+    cfg = synth.CONFIGS[name]
+    inp = synth.make_inputs(cfg)
+    print(f"absorbed vs unabsorbed everywhere {cfg.name}", flush=True)
+    a, _ = run_prefill(cfg, inp)
+    u, _ = run_prefill(cfg, inp, mla.mla_latent_attn_fwd_unabsorbed)
+    a, u = a.float(), u.float()
+    assert torch.isfinite(a).all().item() and torch.isfinite(u).all().item()
+    atol, rtol = TOL[cfg.dtype]
+    bad = (u - a).abs() > 2 * (atol + rtol * a.abs())
+    err = (u - a).abs().max().item()
+    print(f"{cfg.name}: max abs difference {err:.3e} over {a.numel()} elements")
+    assert not bad.any().item(), f"{int(bad.sum().item())} elements differ beyond twice the bar"
 
 
 def test_unabsorbed_bf16_long_prefill_full_size_sampled():
