@@ -1,6 +1,6 @@
 """The calls can be captured into a HIP graph: they allocate nothing, never
 synchronise and record no memset, so a serving loop may capture them once and
-replay them.  Prefill, key-masked prefill and decode are captured once, then
+replay them.  Prefill (absorbed and unabsorbed), key-masked prefill and decode are captured once, then
 replayed several times with new values written into the captured input
 buffers and eager work plus synchronisation between the replays; every replay
 equals the eager call on the same inputs bit for bit."""
@@ -30,10 +30,12 @@ def _setup(what):
     if what == "masked":
         mask = torch.from_numpy(synth.make_key_mask(cfg, p_hole=0.2, lead=3)).cuda()
         return q, lambda: mla.mla_latent_attn_fwd_masked(q, dev["kv_latent"], mask, wk, wv, scale=cfg.scale)
+    if what == "unabsorbed":
+        return q, lambda: mla.mla_latent_attn_fwd_unabsorbed(q, dev["kv_latent"], wk, wv, scale=cfg.scale)
     return q, lambda: mla.mla_latent_attn_fwd(q, dev["kv_latent"], wk, wv, scale=cfg.scale)
 
 
-@pytest.mark.parametrize("what", ["prefill", "masked", "decode"])
+@pytest.mark.parametrize("what", ["prefill", "unabsorbed", "masked", "decode"])
 def test_graph_replays_equal_eager(what):
     import torch
     q, fn = _setup(what)
