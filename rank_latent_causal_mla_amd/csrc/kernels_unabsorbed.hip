@@ -36,6 +36,9 @@ __device__ __forceinline__ void dma_rows32(const uint16_t* base, size_t stride, 
   }
 }
 
+// v = x, written into v's own register (an asm with a tied operand).
+__device__ __forceinline__ void set_in_place(float& v, float x) { asm volatile("v_mov_b32 %0, %1" : "+v"(v) : "v"(x)); }
+
 // f(integral_constant<int, I>) for I = 0 .. N-1, unrolled by construction
 // (a loop this large is not fully unrolled by the compiler, and the softmax
 // pieces need compile-time indices to stay in registers).
@@ -188,12 +191,6 @@ void flash_mha_bf16(const uint16_t* __restrict__ q, const uint16_t* __restrict__
   for (int c = 0; c <= NCB; ++c)
 #pragma unroll
     for (int qb = 0; qb < NQB; ++qb) o[c][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run[NQB], m_thr[NQB];
-#pragma unroll
-  for (int qb = 0; qb < NQB; ++qb) {
-    m_run[qb] = -INFINITY;
-    m_thr[qb] = -INFINITY;
-  }
   // The all-ones A operand of the row-sum ops, produced by an asm so that the
   // compiler keeps it in registers instead of re-creating it next to a matrix
   // op (a VALU write just before a matrix op reads it is a hazard the
@@ -230,6 +227,19 @@ void flash_mha_bf16(const uint16_t* __restrict__ q, const uint16_t* __restrict__
                                             __builtin_bit_cast(u32x2, a1)[0], __builtin_bit_cast(u32x2, a1)[1]});
   };
 
+  // Softmax state of the lane's row in each row block.  Every score chain
+  // starts from cb[qb] = -m_run instead of 0, so the scores arrive relative
+  // to the running maximum and the usual tile needs no subtraction before
+  // its exponentials.
+  //   m_run  the running maximum (absolute; set from tile 0 in the prologue,
+  //          finite from then on since tile 0 holds key 0, visible to every row);
+  //   base   m_run - the reference the scores of the tile being normalised
+  //          started from: 0 except in the tile after a new reference;
+  //   thr    base + slack: a tile maximum above it moves the reference.
+  float m_run[NQB], base[NQB], thr[NQB], cb[NQB][4];
+  bool moved = false;  // wave-uniform: some row moved its reference in the previous tile
+  bool refix = false;  // wave-uniform: the previous tile's probabilities are to be computed again
+
   // tiles 0 and 1 landed (own part), then everyone's
   if (ntiles >= kMhaAhead)
     dma_wait<(kMhaAhead - 2) * NI>();
@@ -255,6 +265,61 @@ void flash_mha_bf16(const uint16_t* __restrict__ q, const uint16_t* __restrict__
 
   // tiles below every row of the wave need no mask
   const int jm = tw0 / kTileKeys < ntiles ? tw0 / kTileKeys : ntiles;
+  // keys of tile j above a row's position to -inf (the caller tests j >= jm)
+  auto mask_tile = [&](int j, f32x4 (&sc)[2][NQB]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb) {
+      const int lim = t_row[qb] - kTileKeys * j - 4 * G;  // last visible key offset 16 kb + u
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (16 * (e >> 2) + (e & 3) > lim) sc[e >> 2][qb][e & 3] = -INFINITY;
+    }
+  };
+  // The probabilities of tile jp again, from its K tile (still in its slot
+  // until the copy two iterations after jp's), relative to the references
+  // jp's iteration moved to (-cb): for the rare tile after which some row's
+  // reference moved or whose scores started from an older reference.
+  auto reprob = [&](int jp, bf16x8 (&P)[NQB]) __attribute__((always_inline)) {
+    f32x4 s2[2][NQB];
+    const uint32_t tslot = (uint32_t)(jp & (kMhaBufs - 1)) * TILE;
+#pragma unroll
+    for (int r = 0; r < 2 * NKS; ++r) {
+      const bf16x8 a = rd_k(tslot, r);
+#pragma unroll
+      for (int qb = 0; qb < NQB; ++qb)
+        s2[r & 1][qb] = mfma16x16x32(a, qf[qb][r >> 1],
+                                     r < 2 ? f32x4{cb[qb][0], cb[qb][1], cb[qb][2], cb[qb][3]} : s2[r & 1][qb]);
+    }
+    if (jp >= jm) mask_tile(jp, s2);
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb) {
+      uint32_t pk2[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        pk2[u] = pack_bf16x2(fast_exp2(s2[u >> 1][qb][2 * (u & 1)]), fast_exp2(s2[u >> 1][qb][2 * (u & 1) + 1]));
+      P[qb] = __builtin_bit_cast(bf16x8, u32x4{pk2[0], pk2[1], pk2[2], pk2[3]});
+    }
+  };
+  // Tile 0 sets the first references: its row maxima (over the four lanes of
+  // a row), its scores made relative to them, and the chains of tile 1 start
+  // from them.
+  if (0 >= jm) mask_tile(0, sA);
+#pragma unroll
+  for (int qb = 0; qb < NQB; ++qb) {
+    float m = fmaxf(fmaxf(fmaxf(sA[0][qb][0], sA[0][qb][1]), fmaxf(sA[0][qb][2], sA[0][qb][3])),
+                    fmaxf(fmaxf(sA[1][qb][0], sA[1][qb][1]), fmaxf(sA[1][qb][2], sA[1][qb][3])));
+    m = fmaxf(m, __shfl_xor(m, 16));
+    m = fmaxf(m, __shfl_xor(m, 32));
+    m_run[qb] = m;
+    base[qb] = 0.f;
+    thr[qb] = kRescaleSlack;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) cb[qb][k] = -m;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) sA[kb][qb][v] -= m;
+  }
   // Iteration j: softmax of tile j (scores in sc, probabilities out in Pn),
   // scores of tile j + 1 into sn, P*V of tile j - 1 from Pp.  Tiles that
   // reach past the wave's first row first get keys above a row's position
@@ -263,17 +328,10 @@ void flash_mha_bf16(const uint16_t* __restrict__ q, const uint16_t* __restrict__
                   bf16x8 (&Pn)[NQB]) __attribute__((always_inline)) {
     const uint32_t kslot = (uint32_t)((j + 1) & (kMhaBufs - 1)) * TILE;                 // scores of tile j + 1
     const uint32_t vslot = (uint32_t)((j > 0 ? j - 1 : 0) & (kMhaBufs - 1)) * TILE;     // P*V of tile j - 1
-    if (j >= jm) {
-#pragma unroll
-      for (int qb = 0; qb < NQB; ++qb) {
-        const int lim = t_row[qb] - kTileKeys * j - 4 * G;  // last visible key offset 16 kb + u
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          if (16 * (e >> 2) + (e & 3) > lim) sc[e >> 2][qb][e & 3] = -INFINITY;
-      }
-    }
+    if (__builtin_expect(refix, 0)) reprob(j - 1, Pp);
+    if (j >= jm) mask_tile(j, sc);
 
-    float mt[NQB], msub[NQB];
+    float mt[NQB];
     bool grow[NQB];
     uint32_t pk[NQB][4];
     // element e = 4 kb + u of row block qb: sc[kb][qb][u]
@@ -314,11 +372,10 @@ void flash_mha_bf16(const uint16_t* __restrict__ q, const uint16_t* __restrict__
         }
       } else if (kp < 32) {  // lazy rescale: a new reference only if the max moved past the slack
         const int qb = kp & 3;
-        grow[qb] = mt[qb] > m_thr[qb];
-        msub[qb] = grow[qb] ? mt[qb] : m_run[qb];
+        grow[qb] = mt[qb] > thr[qb];
       } else if (kp < 64) {  // probability e of row block qb
         const int qb = kp & 3, e = (kp - 32) >> 2;
-        x[qb][e] = fast_exp2(x[qb][e] - msub[qb]);
+        x[qb][e] = fast_exp2(x[qb][e]);
         pin(x[qb][e]);
       } else if (kp < 80) {  // bf16 pairs, then the P operand
         const int qb = kp & 3, u = (kp - 64) >> 2;
@@ -342,7 +399,7 @@ void flash_mha_bf16(const uint16_t* __restrict__ q, const uint16_t* __restrict__
         constexpr int r = i / NQB, qb = i % NQB;
         if constexpr (qb == 0 && r + 2 < NR) kr[(r + 2) % 3] = rd_k(kslot, r + 2);
         if constexpr (r < 2)
-          sn[r & 1][qb] = mfma16x16x32(kr[r % 3], qf[qb][r >> 1], f32x4{0.f, 0.f, 0.f, 0.f});
+          sn[r & 1][qb] = mfma16x16x32(kr[r % 3], qf[qb][r >> 1], f32x4{cb[qb][0], cb[qb][1], cb[qb][2], cb[qb][3]});  // from -ref
         else
           sn[r & 1][qb] = mfma16x16x32(kr[r % 3], qf[qb][r >> 1], sn[r & 1][qb]);
       }
@@ -361,18 +418,38 @@ void flash_mha_bf16(const uint16_t* __restrict__ q, const uint16_t* __restrict__
       __builtin_amdgcn_sched_barrier(0);
     });
 
-    // O and the row sums hold tile j - 1 now: move them to tile j's maxima
-    bool any = false;
+    // The probabilities above are right when every shift is 0: no row of
+    // this tile moved its reference and none did in the previous tile (the
+    // usual case).  Otherwise the state moves to the new references and this
+    // tile's scores are computed again from its K tile (still in its slot,
+    // which is refilled two iterations later), now relative to them.  The
+    // chains of tile j + 1 started from the old cb.
+    bool g = false;
 #pragma unroll
-    for (int qb = 0; qb < NQB; ++qb) any |= grow[qb];
-    if (__builtin_amdgcn_ballot_w64(any)) {
-      float alpha[NQB];
+    for (int qb = 0; qb < NQB; ++qb) g |= grow[qb];
+    const bool grew = __builtin_amdgcn_ballot_w64(g) != 0;
+    float alpha[NQB];
+    refix = false;
+    if (__builtin_expect(grew || moved, 0)) {
 #pragma unroll
       for (int qb = 0; qb < NQB; ++qb) {
-        alpha[qb] = fast_exp2(m_run[qb] - msub[qb]);  // 1 where the reference stayed
-        m_run[qb] = msub[qb];
-        m_thr[qb] = msub[qb] + kRescaleSlack;
+        const float nm = grow[qb] ? mt[qb] + m_run[qb] - base[qb] : m_run[qb];  // the new reference
+        const float nb = nm + cb[qb][0];                                         // tile j + 1 started from cb
+        alpha[qb] = grow[qb] ? fast_exp2(m_run[qb] - nm) : 1.f;
+        // the state is rewritten in place (tied operands): with plain
+        // assignments the compiler kept it in other registers on this path
+        // and copied it back on the usual one
+        set_in_place(m_run[qb], nm);
+        set_in_place(base[qb], nb);
+        set_in_place(thr[qb], nb + kRescaleSlack);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) set_in_place(cb[qb][k], -nm);
       }
+      refix = true;
+    }
+    moved = grew;
+    // O and the row sums hold tile j - 1 now: move them to tile j's maxima
+    if (grew) {
       mfma_agpr_wait();
 #pragma unroll
       for (int c = 0; c <= NCB; ++c)
@@ -404,6 +481,7 @@ void flash_mha_bf16(const uint16_t* __restrict__ q, const uint16_t* __restrict__
 
   // P*V and row sums of the last tile (even counts)
   if (!(ntiles & 1)) {
+    if (refix) reprob(ntiles - 1, PA);
     const uint32_t vslot = (uint32_t)((ntiles - 1) & (kMhaBufs - 1)) * TILE;
 #pragma unroll
     for (int c = 0; c < NCB; ++c) {

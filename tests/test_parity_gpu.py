@@ -93,31 +93,45 @@ def scale_bf16_rows(a, rows, factor):
     return a
 
 
-@pytest.mark.parametrize("masked", [False, True])
-def test_prefill_outlier_keys(masked):
+OUTLIER_CASES = [(300, [37, 150, 151, 298]),   # even tile counts; an outlier in the last tile
+                 (330, [37, 150, 151, 320]),   # the unabsorbed form's last row block has an odd count
+                 (320, [37, 150, 290, 295, 300, 305, 310, 315, 319])]  # outliers across the last tile
+
+
+@pytest.mark.parametrize("case", OUTLIER_CASES, ids=["T300", "T330", "T320"])
+@pytest.mark.parametrize("form", ["absorbed", "masked", "unabsorbed"])
+def test_prefill_outlier_keys(form, case):
     """A few keys with 3x larger latents: the running max of the rows whose
     query points along them jumps past the kernel's 8-unit (log2) rescale
-    slack in a late tile (72 (row, tile) pairs here), while other rows of the
-    same waves do not move -- every row's rescale must follow its own max, not
-    that of a representative lane.  A skipped rescale leaves the earlier keys
-    overweighted by at least 2^8.
+    slack in a late tile (72 (row, tile) pairs at T = 300), while other rows
+    of the same waves do not move -- every row's rescale must follow its own
+    max, not that of a representative lane.  A skipped rescale leaves the
+    earlier keys overweighted by at least 2^8.  In the unabsorbed kernel
+    these are also the only tiles whose probabilities are computed a second
+    time (a moved reference, and the tile after it), including the last
+    tile of a row block with an even and with an odd tile count.
     Bar: logits reach about 15 log2 units here, where the bf16 rounding of
     q_lat alone (2^-9 relative) moves a probability by up to ~1.5%: a model of
     the kernel's four bf16 roundings in float64 puts the worst element at 0.9
     of the 2e-2 bar and the relative RMS error at 3.2e-3, so this test takes
     atol = rtol = 4e-2 and a relative RMS bar of 6e-3."""
     import torch
-    cfg = cfg_like("bf16_prefill", B=2, T=300, H=16)
+    T, rows = case
+    cfg = cfg_like("bf16_prefill", B=2, T=T, H=16)
+    print(f"outlier keys {form} T={T} rows={rows}", flush=True)
     inp = synth.make_inputs(cfg)
-    inp["kv_latent"] = scale_bf16_rows(inp["kv_latent"], [37, 150, 151, 298], 3.0)
+    inp["kv_latent"] = scale_bf16_rows(inp["kv_latent"], rows, 3.0)
     dev = {k: to_device(v) for k, v in inp.items() if k != "seq_lens"}
-    if masked:
+    mask = None
+    if form == "masked":
         mask = synth.make_key_mask(cfg, p_hole=0.1, lead=0)
-        mask[:, [37, 150, 151, 298]] = 1
+        mask[:, rows] = 1
         out = mla.mla_latent_attn_fwd_masked(dev["q"], dev["kv_latent"], torch.from_numpy(mask).cuda(),
                                              dev["w_up_k"], dev["w_up_v"], scale=cfg.scale)
+    elif form == "unabsorbed":
+        out = mla.mla_latent_attn_fwd_unabsorbed(dev["q"], dev["kv_latent"], dev["w_up_k"], dev["w_up_v"],
+                                                 scale=cfg.scale)
     else:
-        mask = None
         out = mla.mla_latent_attn_fwd(dev["q"], dev["kv_latent"], dev["w_up_k"], dev["w_up_v"], scale=cfg.scale)
     torch.cuda.synchronize()
     ref = oracle.latent_attn(inp["q"], inp["kv_latent"], inp["w_up_k"], inp["w_up_v"], cfg.scale, key_mask=mask)
