@@ -123,7 +123,7 @@ void decode_split(const uint16_t* __restrict__ q_lat, const uint16_t* __restrict
       dq = false;
       return;
     }
-    dma_tile32<R>(lat + (size_t)drb * R, dk, dend, dst, w);
+    dma_tile32<R, false, true>(lat + (size_t)drb * R, dk, dend, dst, w);  // each cache row is read once
     dk += kDecodeTileKeys;
     if (dk >= dend) {
       ++db;
