@@ -358,13 +358,14 @@ struct Flash {
   // the 64 matrix ops (a lag of 24 ran 1% faster than 8; 12, 16, 18 and 22
   // were no better than 8).  Scores are in log2 units (q_lat carries
   // scale * log2 e).  With MASK, keys 16 kb + v (from k0 + 4 G) above lim[qb]
-  // are masked.  Returns whether any row's running max moved (then
-  // alpha != 1 for it).
+  // are masked.  Returns whether any row's running max moved; m_old keeps
+  // the maxima before this tile and ps the sums of its probabilities, so that
+  // the rescale factors are computed only when some row moved.
   static constexpr int kPieceLag = 4 * NKS - 40 > 8 ? 4 * NKS - 40 : 8;
   template <bool MASK>
   static __device__ __forceinline__ bool scores_softmax(const char* tile, const bf16x8 (*qf)[NKS], f32x4 (&s)[2][2],
                                                         const f32x4 (&sc)[2][2], const int (&lim)[2], float (&m_run)[2],
-                                                        float (&l_run)[2], float (&alpha)[2], bf16x8 (&P)[2]) {
+                                                        float (&m_old)[2], float (&ps)[2], bf16x8 (&P)[2]) {
     const int lane = threadIdx.x & 63;
     const int G = lane >> 4, n = lane & 15;
     const int f = tswz(n);
@@ -377,7 +378,8 @@ struct Flash {
       const int c = 4 * ks + G;
       return lds_read16(tile + (16 * kb + n) * (R * 2) + 16 * ((c & ~15) | ((c & 15) ^ f)));
     };
-    float x[2][8], mm[2][4], mt[2], ps[2] = {0.f, 0.f}, msub[2];
+    float x[2][8], mm[2][4], mt[2], msub[2];
+    ps[0] = ps[1] = 0.f;
     bool grow[2];
     uint32_t pk[2][4];
     auto piece = [&](int k) {
@@ -404,25 +406,22 @@ struct Flash {
       } else if (k < 12) {  // 8..11: maximum over the four lanes of a row
         const int qb = k & 1;
         mt[qb] = k < 10 ? max_xor16(mt[qb]) : max_xor32(mt[qb]);
-      } else if (k < 14) {  // 12, 13: rescale factor
+      } else if (k < 14) {  // 12, 13: does the reference move
         const int qb = k & 1;
         grow[qb] = mt[qb] > m_run[qb] + kRescaleSlack;
-        alpha[qb] = grow[qb] ? fast_exp2(m_run[qb] - mt[qb]) : 1.f;
       } else if (k < 16) {  // 14, 15: running max
         const int qb = k & 1;
+        m_old[qb] = m_run[qb];
         m_run[qb] = grow[qb] ? mt[qb] : m_run[qb];
         msub[qb] = m_run[qb] == -INFINITY ? 0.f : m_run[qb];
       } else if (k < 32) {  // 16..31: probability u of row block qb, summed in pairs
         const int qb = k & 1, u = (k - 16) >> 1;
         x[qb][u] = fast_exp2(x[qb][u] - msub[qb]);
         if (u & 1) ps[qb] += x[qb][u - 1] + x[qb][u];
-      } else if (k < 40) {  // 32..39: bf16 pairs, then the running sum and the P operand
+      } else if (k < 40) {  // 32..39: bf16 pairs, then the P operand
         const int qb = k & 1, u = (k - 32) >> 1;
         pk[qb][u] = pack_bf16x2(x[qb][2 * u], x[qb][2 * u + 1]);
-        if (u == 3) {
-          l_run[qb] = l_run[qb] * alpha[qb] + ps[qb];
-          P[qb] = __builtin_bit_cast(bf16x8, u32x4{pk[qb][0], pk[qb][1], pk[qb][2], pk[qb][3]});
-        }
+        if (u == 3) P[qb] = __builtin_bit_cast(bf16x8, u32x4{pk[qb][0], pk[qb][1], pk[qb][2], pk[qb][3]});
       }
     };
     constexpr int NR = 2 * NKS, DEPTH = 3;
@@ -550,22 +549,31 @@ void flash_latent_bf16(const uint16_t* __restrict__ q_lat, const uint16_t* __res
       lim[qb] = (COMPACT ? *(const __attribute__((address_space(3))) int*)(uintptr_t)(tbuf + (2 * w + qb) * 64 + lane)
                          : t_row[qb]) - k0 - 4 * G;
     bf16x8 P[2];
-    float alpha[2];
+    float m_old[2], ps[2];
     // scores of tile j + 1 (after the last tile: a stale buffer, discarded)
     // with the softmax of tile j between their matrix ops
     f32x4 s_next[2][2];
     const char* ntile = smem + ((j + 1) % kFlashBufs) * TILE;
     const bool grow = k0 + kTileKeys - 1 > t_first_w
-                          ? F::template scores_softmax<true>(ntile, qf, s_next, s_cur, lim, m_run, l_run, alpha, P)
-                          : F::template scores_softmax<false>(ntile, qf, s_next, s_cur, lim, m_run, l_run, alpha, P);
+                          ? F::template scores_softmax<true>(ntile, qf, s_next, s_cur, lim, m_run, m_old, ps, P)
+                          : F::template scores_softmax<false>(ntile, qf, s_next, s_cur, lim, m_run, m_old, ps, P);
     // every wave passed the barrier that ended iteration j - 1: the exchange buffers are free
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
+    for (int qb = 0; qb < 2; ++qb)
       *(__attribute__((address_space(3))) bf16x8*)(uintptr_t)(pbuf + ((2 * w + qb) * 64 + lane) * 16) = P[qb];
-      if (G == 0) abuf[(2 * w + qb) * 16 + n] = alpha[qb];
-    }
     // every lane votes: a ballot inside the lane-0 branch would see lane 0's row only
     const uint64_t grew = __builtin_amdgcn_ballot_w64(grow);
+    if (grew != 0) {  // rare: rescale factors, posted only by a wave whose rows moved
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        const float alpha = m_old[qb] == m_run[qb] ? 1.f : fast_exp2(m_old[qb] - m_run[qb]);
+        l_run[qb] = l_run[qb] * alpha + ps[qb];
+        if (G == 0) abuf[(2 * w + qb) * 16 + n] = alpha;
+      }
+    } else {
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) l_run[qb] += ps[qb];
+    }
     if (lane == 0) fbuf[w] = grew != 0;
     lds_publish_barrier();  // P and rescale factors of tile j posted
     bf16x8 pq[F::NQ];
@@ -578,7 +586,7 @@ void flash_latent_bf16(const uint16_t* __restrict__ q_lat, const uint16_t* __res
       if ((f[0] | f[1] | f[2] | f[3]) != 0) {  // some row of the block has a new max
         float al[F::NQ];
 #pragma unroll
-        for (int q = 0; q < F::NQ; ++q) al[q] = abuf[q * 16 + n];
+        for (int q = 0; q < F::NQ; ++q) al[q] = f[q >> 1] ? abuf[q * 16 + n] : 1.f;  // row block q: wave q / 2
         mfma_agpr_wait();
 #pragma unroll
         for (int c = 0; c < F::NCW; ++c)
