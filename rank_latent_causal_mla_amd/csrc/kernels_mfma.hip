@@ -358,14 +358,19 @@ struct Flash {
   // the 64 matrix ops (a lag of 24 ran 1% faster than 8; 12, 16, 18 and 22
   // were no better than 8).  Scores are in log2 units (q_lat carries
   // scale * log2 e).  With MASK, keys 16 kb + v (from k0 + 4 G) above lim[qb]
-  // are masked.  Returns whether any row's running max moved; m_old keeps
-  // the maxima before this tile and ps the sums of its probabilities, so that
-  // the rescale factors are computed only when some row moved.
+  // are masked.  A row's reference moves when its tile maximum exceeds thr
+  // (its running maximum plus the slack); the probabilities are taken
+  // relative to msub, the new maximum where grow is set and mref (the
+  // running maximum, or 0 before the row's first visible key) otherwise.
+  // ps returns the sums of the probabilities: the caller updates the state,
+  // the running sums and the rescale factors only when some row moved.
+  // Returns whether any row's reference moved.
   static constexpr int kPieceLag = 4 * NKS - 40 > 8 ? 4 * NKS - 40 : 8;
   template <bool MASK>
   static __device__ __forceinline__ bool scores_softmax(const char* tile, const bf16x8 (*qf)[NKS], f32x4 (&s)[2][2],
-                                                        const f32x4 (&sc)[2][2], const int (&lim)[2], float (&m_run)[2],
-                                                        float (&m_old)[2], float (&ps)[2], bf16x8 (&P)[2]) {
+                                                        const f32x4 (&sc)[2][2], const int (&lim)[2], const float (&thr)[2],
+                                                        const float (&mref)[2], float (&msub)[2], bool (&grow)[2],
+                                                        float (&ps)[2], bf16x8 (&P)[2]) {
     const int lane = threadIdx.x & 63;
     const int G = lane >> 4, n = lane & 15;
     const int f = tswz(n);
@@ -378,9 +383,8 @@ struct Flash {
       const int c = 4 * ks + G;
       return lds_read16(tile + (16 * kb + n) * (R * 2) + 16 * ((c & ~15) | ((c & 15) ^ f)));
     };
-    float x[2][8], mm[2][4], mt[2], msub[2];
+    float x[2][8], mm[2][4], mt[2];
     ps[0] = ps[1] = 0.f;
-    bool grow[2];
     uint32_t pk[2][4];
     auto piece = [&](int k) {
       if (k < 0) {
@@ -408,12 +412,10 @@ struct Flash {
         mt[qb] = k < 10 ? max_xor16(mt[qb]) : max_xor32(mt[qb]);
       } else if (k < 14) {  // 12, 13: does the reference move
         const int qb = k & 1;
-        grow[qb] = mt[qb] > m_run[qb] + kRescaleSlack;
-      } else if (k < 16) {  // 14, 15: running max
+        grow[qb] = mt[qb] > thr[qb];
+      } else if (k < 16) {  // 14, 15: the reference of this tile's probabilities
         const int qb = k & 1;
-        m_old[qb] = m_run[qb];
-        m_run[qb] = grow[qb] ? mt[qb] : m_run[qb];
-        msub[qb] = m_run[qb] == -INFINITY ? 0.f : m_run[qb];
+        msub[qb] = grow[qb] ? mt[qb] : mref[qb];
       } else if (k < 32) {  // 16..31: probability u of row block qb, summed in pairs
         const int qb = k & 1, u = (k - 16) >> 1;
         x[qb][u] = fast_exp2(x[qb][u] - msub[qb]);
@@ -529,7 +531,11 @@ void flash_latent_bf16(const uint16_t* __restrict__ q_lat, const uint16_t* __res
   for (int c = 0; c < F::NCW; ++c)
 #pragma unroll
     for (int q = 0; q < F::NQ; ++q) o[c][q] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // running maximum and sum of the lane's row in each row block; thr =
+  // m_run + slack and mref = m_run (0 while m_run is -inf) are kept as state
+  // so that the usual tile spends no instruction on deriving them
   float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
+  float thr[2] = {-INFINITY, -INFINITY}, mref[2] = {0.f, 0.f};
   const int cw = w * (R / 4);
   const TileCols<R> cols;
 
@@ -549,14 +555,15 @@ void flash_latent_bf16(const uint16_t* __restrict__ q_lat, const uint16_t* __res
       lim[qb] = (COMPACT ? *(const __attribute__((address_space(3))) int*)(uintptr_t)(tbuf + (2 * w + qb) * 64 + lane)
                          : t_row[qb]) - k0 - 4 * G;
     bf16x8 P[2];
-    float m_old[2], ps[2];
+    float msub[2], ps[2];
+    bool growq[2];
     // scores of tile j + 1 (after the last tile: a stale buffer, discarded)
     // with the softmax of tile j between their matrix ops
     f32x4 s_next[2][2];
     const char* ntile = smem + ((j + 1) % kFlashBufs) * TILE;
     const bool grow = k0 + kTileKeys - 1 > t_first_w
-                          ? F::template scores_softmax<true>(ntile, qf, s_next, s_cur, lim, m_run, m_old, ps, P)
-                          : F::template scores_softmax<false>(ntile, qf, s_next, s_cur, lim, m_run, m_old, ps, P);
+                          ? F::template scores_softmax<true>(ntile, qf, s_next, s_cur, lim, thr, mref, msub, growq, ps, P)
+                          : F::template scores_softmax<false>(ntile, qf, s_next, s_cur, lim, thr, mref, msub, growq, ps, P);
     // every wave passed the barrier that ended iteration j - 1: the exchange buffers are free
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb)
@@ -566,7 +573,12 @@ void flash_latent_bf16(const uint16_t* __restrict__ q_lat, const uint16_t* __res
     if (grew != 0) {  // rare: rescale factors, posted only by a wave whose rows moved
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) {
-        const float alpha = m_old[qb] == m_run[qb] ? 1.f : fast_exp2(m_old[qb] - m_run[qb]);
+        const float alpha = growq[qb] ? fast_exp2(m_run[qb] - msub[qb]) : 1.f;
+        if (growq[qb]) {
+          m_run[qb] = msub[qb];
+          thr[qb] = msub[qb] + kRescaleSlack;
+          mref[qb] = msub[qb];
+        }
         l_run[qb] = l_run[qb] * alpha + ps[qb];
         if (G == 0) abuf[(2 * w + qb) * 16 + n] = alpha;
       }
