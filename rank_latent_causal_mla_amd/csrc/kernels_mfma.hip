@@ -588,13 +588,16 @@ void flash_latent_bf16(const uint16_t* __restrict__ q_lat, const uint16_t* __res
     }
     if (lane == 0) fbuf[w] = grew != 0;
     lds_publish_barrier();  // P and rescale factors of tile j posted
+    // The flags first: the branch on them then waits for this read alone (the
+    // LDS counter drains in order), while the P and latent reads behind it
+    // are still in flight.
+    const u32x4 f = *(const __attribute__((address_space(3))) u32x4*)(uintptr_t)fbuf;
     bf16x8 pq[F::NQ];
 #pragma unroll
     for (int q = 0; q < F::NQ; ++q) pq[q] = lds_read16(pbuf + (q * 64 + lane) * 16);
     const char* tile = smem + (j % kFlashBufs) * TILE;
     bf16x8 a_next = cols(tile, cw);
     {
-      const u32x4 f = *(const __attribute__((address_space(3))) u32x4*)(uintptr_t)fbuf;
       if ((f[0] | f[1] | f[2] | f[3]) != 0) {  // some row of the block has a new max
         float al[F::NQ];
 #pragma unroll
