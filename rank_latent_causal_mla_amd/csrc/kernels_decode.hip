@@ -238,32 +238,41 @@ void decode_split(const uint16_t* __restrict__ q_lat, const uint16_t* __restrict
     lds_publish_barrier();  // X: maxima posted; every wave is done with item tau - 1
     // refill the buffer of item tau - 1
     if (!ddone) copy_next();
-    float alpha[2];
+    float m_new[2];
     bool grow_any = false;
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
       const float mt = fmaxf(mxbuf[q * 16 + n], mxbuf[(2 + q) * 16 + n]);
       const bool grow = mt > m_run[q] + kRescaleSlack;
-      alpha[q] = grow ? fast_exp2(m_run[q] - mt) : 1.f;
-      m_run[q] = grow ? mt : m_run[q];
+      m_new[q] = grow ? mt : m_run[q];
       grow_any |= grow;
     }
+    float psum;
     {
-      const float mq = qb ? m_run[1] : m_run[0];
+      const float mq = qb ? m_new[1] : m_new[0];
       const float msub = mq == -INFINITY ? 0.f : mq;
       const float p0 = fast_exp2(x[0] - msub), p1 = fast_exp2(x[1] - msub);
       const float p2 = fast_exp2(x[2] - msub), p3 = fast_exp2(x[3] - msub);
-      l_part = l_part * (qb ? alpha[1] : alpha[0]) + ((p0 + p1) + (p2 + p3));
+      psum = (p0 + p1) + (p2 + p3);
       *(u32x2*)pw = u32x2{pack_bf16x2(p0, p1), pack_bf16x2(p2, p3)};
     }
     // own part of tile tau + 1 landed before the barrier that publishes P
     if (tau + 1 < issued) dma_wait_tiles<NI>(issued - tau - 2);
     lds_publish_barrier();  // Y: P of tile tau complete; tile tau + 1 landed
-    if (__builtin_amdgcn_ballot_w64(grow_any)) {
+    if (__builtin_amdgcn_ballot_w64(grow_any)) {  // rare: rescale factors only now
+      float alpha[2];
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        alpha[q] = m_new[q] == m_run[q] ? 1.f : fast_exp2(m_run[q] - m_new[q]);
+        m_run[q] = m_new[q];
+      }
+      l_part = l_part * (qb ? alpha[1] : alpha[0]) + psum;
 #pragma unroll
       for (int c = 0; c < NCW; ++c)
 #pragma unroll
         for (int q = 0; q < 2; ++q) o[c][q] *= alpha[q];
+    } else {
+      l_part += psum;
     }
     // ---- O^T += L^T P^T over this wave's columns.  Transpose read t of lane
     // (G, n): key 16 t + 4 G + n / 4, columns rw + 16 c + 4 (n % 4) .. + 3.
