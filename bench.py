@@ -137,6 +137,10 @@ def to_device(arr):
 
 # ---------------------------------------------------------------- GPU timing
 MIN_TIMED_CALLS = 50   # calls timed one by one for the median and minimum
+# A decode call lasts about 80 us: its mean is taken over this many calls back
+# to back (16 ms), so the host's lead over the first launches, which a serving
+# loop pays once, does not weigh on it.
+DECODE_TIMED_CALLS = 200
 
 
 def time_steps(fn, steps: int, warmup: int):
@@ -521,7 +525,7 @@ def main(argv=None):
                 "kernels_ms": {k: round(v["avg_ms"], 4) for k, v in fkt.items()}})
     if not args.no_decode:
         dcfg = synth.CONFIGS[args.decode_workload]
-        dms, dkt, lens, ddist = bench_decode(dcfg, max(args.steps, 10), sub_warmup)
+        dms, dkt, lens, ddist = bench_decode(dcfg, max(args.steps, DECODE_TIMED_CALLS), sub_warmup)
         db = decode_bytes(dcfg, lens)
         split = dkt.get("decode_split")
         droof = None
@@ -537,7 +541,7 @@ def main(argv=None):
                           "sum_seq_lens": int(np.sum(lens)), "roofline": droof,
                           "kernels_ms": {k: round(v["avg_ms"], 4) for k, v in dkt.items()}}
         if dcfg.dtype == "bf16":
-            vms, vdist = bench_decode_varlen(dcfg, max(args.steps, 10), sub_warmup)
+            vms, vdist = bench_decode_varlen(dcfg, max(args.steps, DECODE_TIMED_CALLS), sub_warmup)
             line["decode"]["varlen"] = {"what": "the same decode over a packed cache (mla_decode_varlen_fwd)",
                                         "value": round(db["total"] / (vms * 1e-3) / 1e9, 1), "unit": "GB/s",
                                         "ms_per_step": round(vms, 4), "per_call": vdist}

@@ -5,9 +5,10 @@
 // sequence and attends keys 0..L_b-1): every head's r-wide query q_lat
 // attends the shared latents, the online softmax keeps (m, l, o_lat), and
 // o_lat is up-projected per head.  The cache is streamed once from HBM:
-//   decode_prep      -- split plan, absorption and W_uv transpose in one launch;
+//   decode_prep      -- split plan and absorption in one launch;
 //   decode_split     -- split-K over balanced chunks of every sequence; each
-//                       block writes one partial state per head;
+//                       block writes one partial state per head; blocks past
+//                       the split's transpose W_uv for the merge;
 //   decode_merge_up  -- log-sum-exp merge of the partial states of each
 //                       (b, h), then the W_uv up-projection on the matrix unit.
 #include <algorithm>
@@ -56,6 +57,11 @@ __device__ __forceinline__ void dma_wait_tiles(int later) {
 //            the tile's keys in the order 16 t + 4 G + v; A by two transpose reads)
 // Every wave tracks the running maxima of all 32 heads (identical in every
 // wave) and the partial sum l over its own 16 keys of its 16 heads.
+// Blocks 0 .. P * ceil(H / 32) - 1 are the split's (g = index mod P, head group
+// index / P); each later block transposes the 64-wide e strip of one head of
+// W_uv into W_uv^T for the merge.  Those blocks are dispatched after every
+// split block, so they take compute units as the first split blocks finish,
+// in the shadow of the slowest ones.
 __device__ __forceinline__ int decode_chunk(int N, int P) {
   const int C = (N + P - 1) / P;
   return C < 1 ? 1 : C;
@@ -65,13 +71,15 @@ template <int R>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
 void decode_split(const uint16_t* __restrict__ q_lat, const uint16_t* __restrict__ lat,
                   const int32_t* __restrict__ S, const int32_t* __restrict__ RB, uint16_t* __restrict__ part_o,
-                  float* __restrict__ part_ml, int B, int H, int P) {
+                  float* __restrict__ part_ml, int B, int H, int P, const uint16_t* __restrict__ wv,
+                  uint16_t* __restrict__ wvT, int d) {
   constexpr int TILE = kDecodeTileKeys * R * 2;
   constexpr int NI = TILE / 1024 / 4;  // copy instructions per wave and tile
   constexpr int NKS = R / 32;          // contraction steps of a score block
   constexpr int NCW = R / 64;          // 16-column blocks of this wave's quarter
   static_assert(kDecodeBufs == 4, "dma_wait_tiles covers up to 2 later tiles");
   static_assert(NKS % 2 == 0, "two score chains");
+  static_assert(R * 128 <= kDecodeBufs * TILE, "a W_uv strip fits the ring");
   extern __shared__ __attribute__((aligned(16))) char smem[];
   // after the ring: P [2 q][4 G][16 n][2 kb][4] bf16, maxima [2 kb][2 q][16] f32, l likewise
   char* pbuf = smem + kDecodeBufs * TILE;
@@ -82,7 +90,13 @@ void decode_split(const uint16_t* __restrict__ q_lat, const uint16_t* __restrict
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int kb = w >> 1, qb = w & 1;
   const int G = lane >> 4, n = lane & 15;
-  const int g = blockIdx.x, hg = blockIdx.y;
+  const int nsplit = P * ((H + 31) / 32);
+  if ((int)blockIdx.x >= nsplit) {  // block-uniform: a W_uv transpose block
+    const int t = blockIdx.x - nsplit, neb = (d + 63) / 64;
+    transpose_wv_strip<R>(wv, wvT, H, d, t % neb, t / neb, (uint16_t*)smem);
+    return;
+  }
+  const int g = blockIdx.x % P, hg = blockIdx.x / P;
   const int N = S[B];
   const int C = decode_chunk(N, P);
   const int x0 = (int)min((long long)g * C, (long long)N);
@@ -314,27 +328,21 @@ void decode_split(const uint16_t* __restrict__ q_lat, const uint16_t* __restrict
 }
 
 // Prologue of a decode call in one launch (independent block roles):
-//   block 0                  -- the prefix S of the clamped lengths and the row bases RB;
-//   the next nabs blocks     -- absorption, 32 sequences x 128 rho of one head each;
-//   the last ntr blocks      -- the W_uv transpose, 64 x 64 tiles.
+//   block 0          -- the prefix S of the clamped lengths and the row bases RB;
+//   the other blocks -- absorption, 32 sequences x 128 rho of one head each.
+// (The W_uv transpose runs in the tail of decode_split.)
 template <int R, int DK>
 __global__ __launch_bounds__(256) void decode_prep(const uint16_t* __restrict__ q, const uint16_t* __restrict__ wk,
-                                                   uint16_t* __restrict__ q_lat, const uint16_t* __restrict__ wv,
-                                                   uint16_t* __restrict__ wvT, const int32_t* __restrict__ lens,
-                                                   const int32_t* __restrict__ cu, int B, int Tmax, int H, int d,
-                                                   float qscale, int32_t* __restrict__ S, int32_t* __restrict__ RB,
-                                                   int nabs) {
+                                                   uint16_t* __restrict__ q_lat, const int32_t* __restrict__ lens,
+                                                   const int32_t* __restrict__ cu, int B, int Tmax, int H,
+                                                   float qscale, int32_t* __restrict__ S, int32_t* __restrict__ RB) {
   constexpr int NQ = R / 128;
   const int bid = blockIdx.x;
   if (bid == 0) {
     length_prefix_block(lens, cu, B, Tmax, S, RB);
-  } else if (bid <= nabs) {
+  } else {
     const int t = bid - 1;
     absorb_tile<R, DK, 1>(q, wk, q_lat, B, H, qscale, t / (H * NQ), 1, (t / NQ) % H, 128 * (t % NQ));
-  } else {
-    const int t = bid - 1 - nabs;
-    const int nrb = R / kTransposeTile, neb = (d + kTransposeTile - 1) / kTransposeTile;
-    transpose_wv_tile(wv, wvT, R, H, d, t % nrb, (t / nrb) % neb, t / (nrb * neb));
   }
 }
 
@@ -511,11 +519,10 @@ static hipError_t run_decode(const uint16_t* q, const uint16_t* lat, const int32
   {
     ProfScope ps("decode_prep", st);
     const int nabs = ((B + 31) / 32) * H * (R / 128);
-    const int ntr = (R / kTransposeTile) * ((d + kTransposeTile - 1) / kTransposeTile) * H;
-    const dim3 grid(1 + nabs + ntr);
-#define PREP(DK)                                                                                          \
-  hipLaunchKernelGGL((decode_prep<R, DK>), grid, dim3(256), 0, st, q, wk, q_lat, wv, wvT, lens, cu, B, Tmax, H, \
-                     d, sl2, S, RB, nabs)
+    const dim3 grid(1 + nabs);
+#define PREP(DK)                                                                                               \
+  hipLaunchKernelGGL((decode_prep<R, DK>), grid, dim3(256), 0, st, q, wk, q_lat, lens, cu, B, Tmax, H, sl2, S, \
+                     RB)
     switch (d) {
       case 32: PREP(2); break;
       case 64: PREP(4); break;
@@ -527,8 +534,9 @@ static hipError_t run_decode(const uint16_t* q, const uint16_t* lat, const int32
   }
   {
     ProfScope ps("decode_split", st);
-    hipLaunchKernelGGL(decode_split<R>, dim3(P, nhg), dim3(256), lds, st, q_lat, lat, S, RB, part_o, part_ml, B, H,
-                       P);
+    const int ntr = ((d + 63) / 64) * H;  // one W_uv transpose block per head and 64-wide e strip
+    hipLaunchKernelGGL(decode_split<R>, dim3(P * nhg + ntr), dim3(256), lds, st, q_lat, lat, S, RB, part_o, part_ml,
+                       B, H, P, wv, wvT, d);
   }
   {
     ProfScope ps("decode_merge_up", st);

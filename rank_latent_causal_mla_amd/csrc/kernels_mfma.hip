@@ -151,7 +151,8 @@ __global__ __launch_bounds__(256, 2) void absorb_bf16(const uint16_t* __restrict
 
 __global__ __launch_bounds__(256) void transpose_wv(const uint16_t* __restrict__ wv, uint16_t* __restrict__ wvT,
                                                     int R, int H, int d) {
-  transpose_wv_tile(wv, wvT, R, H, d, blockIdx.x, blockIdx.y, blockIdx.z);
+  __shared__ __attribute__((aligned(16))) TransposeRow tile[kTransposeTile];
+  transpose_wv_tile(wv, wvT, R, H, d, blockIdx.x, blockIdx.y, blockIdx.z, tile);
 }
 
 template <int R>

@@ -62,12 +62,14 @@ __device__ __forceinline__ void absorb_tile(const uint16_t* __restrict__ q, cons
 
 // W_uv [R, H, d] -> W_uv^T [H, d, R], so the up-projection reads rho-contiguous
 // rows.  The block transposes the 64 x 64 tile (rho block rb, e block eb) of
-// head h through LDS, reading and writing 16-byte pieces (d and R are
-// multiples of 32 and 64 on this path; e past d is skipped).
+// head h through the LDS array `tile` (16-byte aligned), reading and writing
+// 16-byte pieces (d and R are multiples of 32 and 64 on this path; e past d
+// is skipped).
 constexpr int kTransposeTile = 64;
+typedef uint16_t TransposeRow[kTransposeTile + 8];
 __device__ __forceinline__ void transpose_wv_tile(const uint16_t* __restrict__ wv, uint16_t* __restrict__ wvT,
-                                                  int R, int H, int d, int rb, int eb, int h) {
-  __shared__ __attribute__((aligned(16))) uint16_t tile[64][64 + 8];
+                                                  int R, int H, int d, int rb, int eb, int h,
+                                                  TransposeRow* tile) {
   const int rho0 = rb * 64, e0 = eb * 64;
   const int tid = threadIdx.x;
   // read: 64 rho rows x 8 pieces of 8 e
@@ -91,6 +93,46 @@ __device__ __forceinline__ void transpose_wv_tile(const uint16_t* __restrict__ w
     for (int i = 0; i < 4; ++i)
       w4[i] = (uint32_t)tile[8 * c + 2 * i][er] | ((uint32_t)tile[8 * c + 2 * i + 1][er] << 16);
     *(u32x4*)(wvT + ((size_t)h * d + e) * R + rho0 + 8 * c) = u32x4{w4[0], w4[1], w4[2], w4[3]};
+  }
+}
+
+// The same transpose for all R rho of head h and e in [64 eb, 64 eb + 64),
+// every load in flight before the first LDS write, through `tile` (R x 128
+// bytes of LDS, 16-byte aligned).  Piece (rho, c) of 8 e sits at chunk
+// c ^ ((rho / 8) % 8) of its 128-byte row, so both the row writes and the
+// column reads below are free of bank conflicts; each store instruction
+// writes 8 W_uv^T rows x 128 contiguous bytes.
+template <int R>
+__device__ __forceinline__ void transpose_wv_strip(const uint16_t* __restrict__ wv, uint16_t* __restrict__ wvT,
+                                                   int H, int d, int eb, int h, uint16_t* tile) {
+  constexpr int NP = R * 8 / 256;  // 16-byte pieces per thread, R rows x 8 pieces
+  const int e0 = eb * 64, tid = threadIdx.x;
+  u32x4 v[NP];
+#pragma unroll
+  for (int k = 0; k < NP; ++k) {
+    const int idx = tid + 256 * k, r = idx >> 3, c = idx & 7;
+    const int e = e0 + 8 * c;
+    v[k] = e < d ? *(const u32x4*)(wv + ((size_t)r * H + h) * d + e) : u32x4{0, 0, 0, 0};
+  }
+#pragma unroll
+  for (int k = 0; k < NP; ++k) {
+    const int idx = tid + 256 * k, r = idx >> 3, c = idx & 7;
+    *(u32x4*)(tile + r * 64 + 8 * (c ^ ((r >> 3) & 7))) = v[k];
+  }
+  __syncthreads();
+  // output pieces: e row er, rho [8 c, 8 c + 8); a wave takes 8 rows x 8 pieces
+#pragma unroll
+  for (int k = 0; k < NP; ++k) {
+    const int idx = tid + 256 * k, grp = idx >> 6, l = idx & 63;
+    const int er = 8 * (grp & 7) + (l >> 3), c = 8 * (grp >> 3) + (l & 7);
+    const int e = e0 + er;
+    if (e >= d) continue;
+    const uint16_t* col = tile + 8 * ((er >> 3) ^ (c & 7)) + (er & 7);
+    uint32_t w4[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      w4[i] = (uint32_t)col[(8 * c + 2 * i) * 64] | ((uint32_t)col[(8 * c + 2 * i + 1) * 64] << 16);
+    *(u32x4*)(wvT + ((size_t)h * d + e) * R + 8 * c) = u32x4{w4[0], w4[1], w4[2], w4[3]};
   }
 }
 
