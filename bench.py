@@ -141,6 +141,9 @@ MIN_TIMED_CALLS = 50   # calls timed one by one for the median and minimum
 # to back (16 ms), so the host's lead over the first launches, which a serving
 # loop pays once, does not weigh on it.
 DECODE_TIMED_CALLS = 200
+# Likewise the sub-millisecond prefill workloads (bf16_prefill, the full
+# paths): at least this many calls (about 45 ms at bf16_prefill).
+SHORT_TIMED_CALLS = 60
 
 
 def time_steps(fn, steps: int, warmup: int):
@@ -443,10 +446,10 @@ def main(argv=None):
         # the shorter bf16 prefill workload (B=8, T=2048, H=16): the same kernels at a length where each query
         # block carries 8x less work, so fixed costs per block weigh more
         scfg = synth.CONFIGS["bf16_prefill"]
-        sms, skt, _, sdist = bench_prefill(scfg, args.steps, sub_warmup)
+        sms, skt, _, sdist = bench_prefill(scfg, max(args.steps, SHORT_TIMED_CALLS), sub_warmup)
         sw = prefill_flops(scfg)
         sfl = skt.get("flash_latent_bf16")
-        ums_s, _, _, _ = bench_prefill(scfg, args.steps, sub_warmup, unabsorbed=True)
+        ums_s, _, _, _ = bench_prefill(scfg, max(args.steps, SHORT_TIMED_CALLS), sub_warmup, unabsorbed=True)
         line["prefill_short"] = {
             "workload": scfg.name, "value": round(sw["total"] / (sms * 1e-3) / 1e12, 2), "unit": "TFLOP/s",
             "ms_per_step": round(sms, 4), "per_call": sdist, "flops_per_step": sw["total"],
@@ -498,7 +501,7 @@ def main(argv=None):
         line["full_path"] = []
         for fcfg in (synth.CONFIGS["fp32_full_path"],
                      dataclasses.replace(synth.CONFIGS["bf16_prefill"], name="bf16_prefill_down1024", D=1024)):
-            fms, fkt, fdist = bench_full(fcfg, args.steps, sub_warmup)
+            fms, fkt, fdist = bench_full(fcfg, max(args.steps, SHORT_TIMED_CALLS), sub_warmup)
             fw = prefill_flops(fcfg)
             down = fkt.get("down_bf16") or fkt.get("down_f32")
             if fcfg.dtype == "bf16":
