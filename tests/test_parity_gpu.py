@@ -346,6 +346,7 @@ DECODE_SMALL = [
     ("bf16_decode", dict(B=3, T=700, H=16, d=256), [700, 1, 333]),     # d = 256
     ("bf16_decode", dict(B=2, T=300, H=32, d=64, r=256), [300, 129]),  # d = 64, r = 256
     ("bf16_decode", dict(B=3, T=200, H=12, d=32, r=128), [200, 5, 64]),  # d = 32 (half a W_uv strip), r = 128
+    ("bf16_decode", dict(B=2, T=90, H=40, d=256, r=256), [90, 33]),  # two head groups, two W_uv strips a head
     ("fp32_small", dict(B=3, T=70, decode=True), [70, 1, 33]),         # float32 decode
 ]
 
